@@ -1,0 +1,281 @@
+/*
+ * attn_oracle.c -- plain fp64 reference for fused scaled-dot-product attention
+ * forward (prefill and split-K decode) and for the split-K log-sum-exp combine.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg load this library.  It shares no code, header, table or
+ * helper with the HIP path, and the HIP path never calls it.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [Neptune notes]  "Neptune论文浅读：把FlashAttention式融合放进编译器"
+ *                    (gentlecold.top, notes on the Neptune PLDI 2026 paper)
+ *   [CANN FA post]   "CANN FlashAttention 不是算力加速器，它在昇腾NPU上做的是
+ *                    '偷懒'的数学" (ai6s.net)
+ *   [Mirage lecture] CMU 15-779 Lecture 11, "Advanced ML Compilation: ML
+ *                    Superoptimization (Mirage)" (semidirectx.com)
+ *
+ * What is computed is the plain definition, not the fused algorithm.  Both the
+ * rolling update and the split-K update reach this result exactly in real
+ * arithmetic ([Neptune notes] section 4: the repair h(t,r,r') = t*exp(r - r')
+ * distributes over the sum; [CANN FA post] section on the online softmax: the
+ * one-pass result equals the two-pass one), so the reference is the definition
+ * itself, evaluated in fp64:
+ *
+ *   [Neptune notes] section 2: the chain QK^T -> score/mask/bias -> softmax -> .V,
+ *   and the stable softmax  softmax(x_j) = exp(x_j - m) / sum_k exp(x_k - m),
+ *   m = max_k x_k.
+ *   [CANN FA post] `softmax_standard`: find the max first, then the exponentials
+ *   and their sum, then normalise (two passes over the row).
+ *
+ * For every output row (b, h, i):
+ *   kv head        hk = h / (Hq / Hkv)      (contiguous query-head groups; the
+ *                  GQA case of [Mirage lecture] section 7.1 has each group of
+ *                  query heads share one K, V pair)
+ *   position       p  = i + (Lk - Lq)       (queries aligned to the end of the
+ *                  keys: a decode query sees the whole cache)
+ *   visible keys   all j, or j <= p when causal
+ *   score          s_j = scale * sum_d q[d] k_j[d] + bias(b, h, i, j)
+ *                  bias: none; dense tensor (element strides, 0 = broadcast);
+ *                  or ALiBi  -slope[h] * |p - j|
+ *   pass 1         m = max_j s_j
+ *   pass 2         l = sum_j exp(s_j - m);  o = sum_j exp(s_j - m) v_j
+ *   output         O = o / l,  LSE = m + ln(l)  (natural log)
+ *   no visible key O = 0, LSE = -inf.
+ *
+ * Inputs are fp32 arrays holding the stored element values exactly (bf16
+ * values widen exactly to fp32); every product and sum is done in double.
+ * Threads split the rows; each thread keeps one row of scores (Lk doubles).
+ * The per-row arithmetic does not depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_BIAS_NONE 0
+#define ORACLE_BIAS_DENSE 1
+#define ORACLE_BIAS_ALIBI 2
+
+typedef struct {
+    int64_t B, Hq, Hkv, Lq, Lk, D;
+    const float *q, *k, *v;
+    double scale;
+    int causal;
+    int bias_kind;
+    const float *bias;
+    int64_t bias_strides[4];
+    const float *slopes;
+    const int64_t *rows;
+    int64_t nrows;
+    double *o, *lse;
+    int64_t next_row;          /* shared work counter */
+    pthread_mutex_t lock;
+} oracle_job;
+
+/* One output row, two passes over its visible keys. */
+static void oracle_row(const oracle_job *J, int64_t flat, double *o, double *lse, double *s)
+{
+    const int64_t i = flat % J->Lq;
+    const int64_t h = (flat / J->Lq) % J->Hq;
+    const int64_t b = flat / (J->Lq * J->Hq);
+    const int64_t G = J->Hq / J->Hkv;
+    const int64_t hk = h / G;
+    const int64_t D = J->D;
+    const int64_t p = i + (J->Lk - J->Lq);
+
+    const float *qrow = J->q + ((b * J->Hq + h) * J->Lq + i) * D;
+    const float *kbase = J->k + (b * J->Hkv + hk) * J->Lk * D;
+    const float *vbase = J->v + (b * J->Hkv + hk) * J->Lk * D;
+
+    int64_t nvis = J->Lk;
+    if (J->causal) {
+        nvis = p + 1;
+        if (nvis < 0) nvis = 0;
+        if (nvis > J->Lk) nvis = J->Lk;
+    }
+
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    if (nvis == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+
+    /* scores of the visible keys */
+    for (int64_t j = 0; j < nvis; ++j) {
+        const float *krow = kbase + j * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (double)krow[d];
+        double sj = J->scale * dot;
+        if (J->bias_kind == ORACLE_BIAS_DENSE) {
+            const int64_t *st = J->bias_strides;
+            sj += (double)J->bias[b * st[0] + h * st[1] + i * st[2] + j * st[3]];
+        } else if (J->bias_kind == ORACLE_BIAS_ALIBI) {
+            double dist = (double)(p - j);
+            if (dist < 0) dist = -dist;
+            sj += -(double)J->slopes[h] * dist;
+        }
+        s[j] = sj;
+    }
+
+    /* pass 1: the row maximum */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j)
+        if (s[j] > m) m = s[j];
+    if (m == -INFINITY) {          /* every visible score is -inf (a -inf bias) */
+        *lse = -INFINITY;
+        return;
+    }
+
+    /* pass 2: exponentials, their sum, and the weighted sum of values */
+    double l = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const double e = exp(s[j] - m);
+        l += e;
+        const float *vrow = vbase + j * D;
+        for (int64_t d = 0; d < D; ++d) o[d] += e * (double)vrow[d];
+    }
+
+    /* normalise */
+    for (int64_t d = 0; d < D; ++d) o[d] /= l;
+    *lse = m + log(l);
+}
+
+static void *oracle_worker(void *arg)
+{
+    oracle_job *J = (oracle_job *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(J->Lk > 0 ? J->Lk : 1));
+    if (!s) return (void *)1;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        const int64_t r = J->next_row;
+        J->next_row += 1;
+        pthread_mutex_unlock(&J->lock);
+        if (r >= J->nrows) break;
+        const int64_t flat = J->rows ? J->rows[r] : r;
+        oracle_row(J, flat, J->o + r * J->D, J->lse + r, s);
+    }
+    free(s);
+    return 0;
+}
+
+/*
+ * oracle_attention: O and LSE for the requested rows.
+ *   q [B,Hq,Lq,D], k and v [B,Hkv,Lk,D]: contiguous fp32.
+ *   scale: the softmax scale (pass the fp32 value the device receives).
+ *   bias_kind 0 none / 1 dense (bias + strides in elements, b,h,i,j) / 2 ALiBi (slopes[Hq]).
+ *   rows: flat row ids (b*Hq + h)*Lq + i, or NULL for all B*Hq*Lq rows in order.
+ *   o [nrows][D] and lse [nrows] are written in fp64.
+ * Returns 0 on success, -1 on an invalid argument, -2 when out of memory.
+ */
+int oracle_attention(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                     const float *q, const float *k, const float *v,
+                     double scale, int causal,
+                     int bias_kind, const float *bias, const int64_t *bias_strides,
+                     const float *slopes,
+                     const int64_t *rows, int64_t nrows,
+                     double *o, double *lse, int nthreads)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || Lq < 0 || Lk < 0 || D < 1) return -1;
+    if (Hq % Hkv != 0) return -1;
+    if (!o || !lse) return -1;
+    if ((Lq > 0 && !q) || (Lk > 0 && (!k || !v))) return -1;
+    if (bias_kind == ORACLE_BIAS_DENSE && (!bias || !bias_strides)) return -1;
+    if (bias_kind == ORACLE_BIAS_ALIBI && !slopes) return -1;
+    if (bias_kind < 0 || bias_kind > 2) return -1;
+
+    const int64_t total = B * Hq * Lq;
+    if (!rows) nrows = total;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= total) return -1;
+
+    oracle_job J;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Lq = Lq; J.Lk = Lk; J.D = D;
+    J.q = q; J.k = k; J.v = v;
+    J.scale = scale; J.causal = causal;
+    J.bias_kind = bias_kind; J.bias = bias; J.slopes = slopes;
+    for (int t = 0; t < 4; ++t) J.bias_strides[t] = bias_strides ? bias_strides[t] : 0;
+    J.rows = rows; J.nrows = nrows;
+    J.o = o; J.lse = lse;
+    J.next_row = 0;
+    pthread_mutex_init(&J.lock, 0);
+
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+
+    int rc = 0;
+    if (nthreads == 1) {
+        if (oracle_worker(&J)) rc = -2;
+    } else {
+        pthread_t th[256];
+        int started = 0;
+        for (int t = 0; t < nthreads; ++t) {
+            if (pthread_create(&th[t], 0, oracle_worker, &J) != 0) break;
+            ++started;
+        }
+        if (started == 0 && oracle_worker(&J)) rc = -2;
+        for (int t = 0; t < started; ++t) {
+            void *ret = 0;
+            pthread_join(th[t], &ret);
+            if (ret) rc = -2;
+        }
+    }
+    pthread_mutex_destroy(&J.lock);
+    return rc;
+}
+
+/*
+ * oracle_splitk_combine: the global step of the split-K update, in fp64.
+ *
+ * [Neptune notes] section 6: the key dimension is split into local reductions
+ * whose max, sum and output are computed independently; the global step
+ * repairs each local sum and output with the global max and adds them up.
+ * With the repair term of section 4, h(t, r, r') = t * exp(r - r'):
+ *
+ *   M   = max_s m_s
+ *   w_s = exp(m_s - M)          (0 for a chunk with no key: m_s = -inf)
+ *   L   = sum_s w_s l_s
+ *   O   = sum_s w_s o_s / L,    LSE = M + ln L
+ *   a row with L == 0 (no key anywhere) gives O = 0 and LSE = -inf.
+ *
+ * o_part [rows][S][D], m_part and l_part [rows][S]: o_s = sum_j exp(s_j - m_s) v_j
+ * and l_s = sum_j exp(s_j - m_s) over chunk s; m_s may be any finite reference
+ * value (the result does not depend on it, [Mirage lecture] section 5.5).
+ */
+int oracle_splitk_combine(int64_t rows, int64_t S, int64_t D,
+                          const float *o_part, const float *m_part, const float *l_part,
+                          double *o, double *lse)
+{
+    if (rows < 0 || S < 1 || D < 1) return -1;
+    if (rows > 0 && (!o_part || !m_part || !l_part || !o || !lse)) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        double M = -INFINITY;
+        for (int64_t s = 0; s < S; ++s) {
+            const double ms = (double)m_part[r * S + s];
+            if (ms > M) M = ms;
+        }
+        double *orow = o + r * D;
+        for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+        if (M == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double L = 0.0;
+        for (int64_t s = 0; s < S; ++s) {
+            const double ms = (double)m_part[r * S + s];
+            if (ms == -INFINITY) continue;
+            const double w = exp(ms - M);
+            L += w * (double)l_part[r * S + s];
+            const float *os = o_part + (r * S + s) * D;
+            for (int64_t d = 0; d < D; ++d) orow[d] += w * (double)os[d];
+        }
+        if (L == 0.0) {
+            for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
+        for (int64_t d = 0; d < D; ++d) orow[d] /= L;
+        lse[r] = M + log(L);
+    }
+    return 0;
+}

@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module holds no attention arithmetic: it only draws the Q, K, V tensors and
+the bias inputs that both the HIP path and the fp64 oracle consume.  Neither side
+imports the other; both take their inputs from here.
+
+Recipe (one stream per tensor):
+  * Q, K, V ~ N(0, 1), drawn in fp32 by ``torch.randn`` from a ``torch.Generator``
+    seeded with ``seed * 16 + tensor_id`` (Q = 0, K = 1, V = 2, dense bias = 3),
+    then rounded to bf16 (round-to-nearest-even, torch's cast) when the
+    workload's dtype is bf16.  The oracle receives the stored values widened
+    exactly to fp32/fp64.
+  * Small cases are drawn on the CPU and copied to the GPU.  Full-size cases may
+    be drawn directly on the GPU with a CUDA generator (same recipe, different
+    stream); the oracle then gets a host copy of exactly those stored values.
+  * ALiBi slopes follow the workload definition slope_h = 2^(-8 (h + 1) / H),
+    h counted from 0.
+
+The workloads are shape stand-ins for the attention variants of the Neptune
+notes (section 9: Global, Causal, ALiBi and GQA, prefill and decode, sequence
+lengths 128-32768) and the Twill review's forward benchmark shape (B=4, H=32,
+d=128).  No dataset is involved.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import torch
+
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_BIAS = 0, 1, 2, 3
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention problem: shapes, dtype and the score modifiers."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    D: int
+    dtype: str = "bf16"          # "bf16" or "f32": element type of Q, K, V
+    causal: bool = False
+    bias: str = "none"           # "none", "alibi" (slopes) or "dense" (tensor)
+    seed: int = 0
+    scale: Optional[float] = None  # None -> 1/sqrt(D) rounded to fp32
+    splits: Optional[int] = None   # decode only: number of KV chunks
+    extra: dict = field(default_factory=dict, compare=False)
+
+    def softmax_scale(self) -> float:
+        s = self.scale if self.scale is not None else self.D ** -0.5
+        return float(torch.tensor(s, dtype=torch.float32).item())
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads named for this build (sizes as stated there).
+C1_TINY = Workload("tiny-f32-L256-d64", 1, 1, 1, 256, 256, 64, "f32", False, "none", 1001)
+C2_CAUSAL = Workload("causal-prefill-bf16-B4-H32-L4096-d128", 4, 32, 32, 4096, 4096, 128,
+                     "bf16", True, "none", 1002)
+C3_ALIBI = Workload("alibi-causal-prefill-bf16-B2-H16-L8192-d128", 2, 16, 16, 8192, 8192, 128,
+                    "bf16", True, "alibi", 1003)
+C4_DECODE = Workload("decode-splitk-gqa-bf16-B16-Hq32-Hkv8-Lk32768-d128", 16, 32, 8, 1, 32768,
+                     128, "bf16", False, "none", 1004, splits=32)
+C5_PREFILL = Workload("long-causal-prefill-bf16-B1-H8-L32768-d128", 1, 8, 8, 32768, 32768, 128,
+                      "bf16", True, "none", 1005)
+C5_DECODE = Workload("long-decode-bf16-B1-H8-Lk32768-d128", 1, 8, 8, 1, 32768, 128,
+                     "bf16", False, "none", 1005)
+
+WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PREFILL, C5_DECODE)}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def _gen(seed: int, tensor_id: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 16 + int(tensor_id))
+    return g
+
+
+def normal(shape, seed: int, tensor_id: int, dtype: str = "bf16", device="cpu") -> torch.Tensor:
+    """N(0,1) tensor of ``shape`` in the stored dtype (fp32 draw, then RNE cast)."""
+    x = torch.randn(tuple(shape), generator=_gen(seed, tensor_id, device), device=device,
+                    dtype=torch.float32)
+    return x.to(torch_dtype(dtype))
+
+
+def alibi_slopes(H: int) -> torch.Tensor:
+    """slope_h = 2^(-8 (h+1) / H) for h = 0..H-1, as fp32 (CPU)."""
+    h = torch.arange(H, dtype=torch.float64)
+    return torch.pow(2.0, -8.0 * (h + 1.0) / H).to(torch.float32)
+
+
+def make_qkv(w: Workload, device="cpu"):
+    """Q [B,Hq,Lq,D], K and V [B,Hkv,Lk,D] in the workload's dtype on ``device``."""
+    q = normal((w.B, w.Hq, w.Lq, w.D), w.seed, TENSOR_Q, w.dtype, device)
+    k = normal((w.B, w.Hkv, w.Lk, w.D), w.seed, TENSOR_K, w.dtype, device)
+    v = normal((w.B, w.Hkv, w.Lk, w.D), w.seed, TENSOR_V, w.dtype, device)
+    return q, k, v
+
+
+def make_dense_bias(w: Workload, shape=None, dtype: str = "f32", device="cpu") -> torch.Tensor:
+    """A random additive bias, N(0,1), default shape [Hq, Lq, Lk] (broadcast over B)."""
+    shape = shape if shape is not None else (w.Hq, w.Lq, w.Lk)
+    return normal(shape, w.seed, TENSOR_BIAS, dtype, device)

@@ -1,0 +1,567 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is checked against things other than itself:
+
+* the 2x4 max / exp / sum worked example of "Neptune论文浅读" section 3, with
+  closed-form values (tests/golden/softmax_2x4.json), run through the three
+  printed program shapes (three loops, naive fusion, repaired fusion) and
+  through the oracle with scores set to the example row;
+* the online softmax of the CANN FlashAttention post (section on the online
+  softmax), in its corrected reading, against the two-pass form;
+* invariants fixed by the stable-softmax definition (Neptune notes section 2):
+  rows of the softmax sum to 1, constant V gives constant O, a constant bias
+  shifts LSE and leaves O alone, Q = 0 gives the mean of the visible values with
+  LSE = ln(count), causal row 0 returns v_0;
+* an exact case: two keys with bias (0, ln 3) give weights (1/4, 3/4);
+* brute force: the full score matrix through scipy's softmax and logsumexp
+  (a library routine) at N <= 64, covering scale, causal alignment with
+  Lq != Lk, GQA, ALiBi and dense bias;
+* large logits stay finite (Mirage lecture section 5.5: q and K scaled by 40);
+* the split-K combine against the unsplit oracle over several chunkings, with
+  arbitrary per-chunk reference values ("subtracting any m gives the same",
+  Mirage lecture section 5.5) and empty chunks;
+* planted mistakes: copies of the oracle with a plausible error each (wrong kv
+  head, dropped scale, bias sign, causal off-by-one, log base, combine weight)
+  are compiled and must fail these pins.
+"""
+import json
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp, softmax
+
+import oracle
+
+RNG = np.random.default_rng(20261202)
+
+
+# ----------------------------------------------------------------------------
+# independent brute force: full score matrix through scipy
+# ----------------------------------------------------------------------------
+def brute(q, k, v, scale, causal=False, bias=None, slopes=None):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    kk = np.repeat(k, G, axis=1)
+    vv = np.repeat(v, G, axis=1)
+    S = scale * np.matmul(q, np.swapaxes(kk, -1, -2))
+    pos = np.arange(Lq)[:, None] + (Lk - Lq)
+    keys = np.arange(Lk)[None, :]
+    if bias is not None:
+        S = S + np.asarray(bias, dtype=np.float64)
+    if slopes is not None:
+        S = S - np.asarray(slopes, dtype=np.float64)[None, :, None, None] * np.abs(pos - keys)
+    if causal:
+        S = np.where(keys > pos, -np.inf, S)
+    lse = logsumexp(S, axis=-1)
+    empty = np.isneginf(lse)
+    S_safe = np.where(empty[..., None], 0.0, S)
+    P = softmax(S_safe, axis=-1)
+    P = np.where(empty[..., None], 0.0, P)
+    O = np.matmul(P, vv)
+    return O, lse
+
+
+def rnd(*shape, scale=1.0):
+    return (RNG.standard_normal(shape) * scale).astype(np.float32)
+
+
+def assert_close(a, b, tol, what=""):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), what + ": infinity pattern differs"
+    assert np.array_equal(a[~fin], b[~fin]), what + ": infinite values differ"
+    if fin.any():
+        err = np.max(np.abs(a[fin] - b[fin]))
+        assert err <= tol, "%s: max abs err %.3e > %.1e" % (what, err, tol)
+
+
+# ----------------------------------------------------------------------------
+# Neptune notes section 3: the 2x4 example, three program shapes
+# ----------------------------------------------------------------------------
+def three_loop(inp):
+    """max loop, then exp loop, then sum loop (three separate loops)."""
+    n, m = len(inp), len(inp[0])
+    xmax = [-math.inf] * n
+    for i in range(n):
+        for j in range(m):
+            xmax[i] = max(xmax[i], inp[i][j])
+    xexp = [[math.exp(inp[i][j] - xmax[i]) for j in range(m)] for i in range(n)]
+    xsum = [0.0] * n
+    for i in range(n):
+        for j in range(m):
+            xsum[i] += xexp[i][j]
+    return xmax, xsum
+
+
+def naive_fused(inp):
+    """exp and sum moved into the max loop without any repair (wrong in general)."""
+    n, m = len(inp), len(inp[0])
+    xmax = [-math.inf] * n
+    xsum = [0.0] * n
+    for i in range(n):
+        for j in range(m):
+            xmax[i] = max(xmax[i], inp[i][j])
+            xsum[i] += math.exp(inp[i][j] - xmax[i])
+    return xmax, xsum
+
+
+def repaired_fused(inp):
+    """the fused loop keeping the previous and current max and repairing the sum
+    by exp(previous max - current max)."""
+    n, m = len(inp), len(inp[0])
+    xmax, xsum = [0.0] * n, [0.0] * n
+    for i in range(n):
+        prev, acc = -math.inf, 0.0
+        for j in range(m):
+            cur = max(prev, inp[i][j])
+            acc = math.exp(prev - cur) * acc + math.exp(inp[i][j] - cur)
+            prev = cur
+        xmax[i], xsum[i] = prev, acc
+    return xmax, xsum
+
+
+@pytest.fixture(scope="module")
+def ex2x4(golden_dir):
+    with open(os.path.join(golden_dir, "softmax_2x4.json")) as f:
+        return json.load(f)
+
+
+def test_golden_2x4_closed_form_digits(ex2x4):
+    closed = (1 - math.exp(-4)) / (1 - math.exp(-1))
+    for s in ex2x4["xsum"]:
+        assert abs(s - closed) <= 1e-15
+    assert abs(ex2x4["lse"][0] - (3 + math.log(closed))) <= 1e-15
+
+
+def test_2x4_three_loop_matches_closed_form(ex2x4):
+    xmax, xsum = three_loop(ex2x4["inp"])
+    assert xmax == ex2x4["xmax"]
+    for a, b in zip(xsum, ex2x4["xsum"]):
+        assert abs(a - b) <= 1e-15
+
+
+def test_2x4_naive_fusion_is_wrong_when_max_grows(ex2x4):
+    _, xsum = naive_fused(ex2x4["inp"])
+    assert xsum[0] == ex2x4["naive_fused_xsum"][0] == 4.0
+    assert abs(xsum[0] - ex2x4["xsum"][0]) > 2.0
+    assert abs(xsum[1] - ex2x4["naive_fused_xsum"][1]) <= 1e-15
+
+
+def test_2x4_repaired_fusion_equals_three_loop(ex2x4):
+    xmax, xsum = repaired_fused(ex2x4["inp"])
+    assert xmax == ex2x4["xmax"]
+    for a, b in zip(xsum, ex2x4["xsum"]):
+        assert abs(a - b) <= 1e-15 * b
+
+
+def test_2x4_repaired_fusion_random_rows():
+    inp = RNG.standard_normal((2, 4)).tolist()
+    _, s3 = three_loop(inp)
+    _, sr = repaired_fused(inp)
+    for a, b in zip(sr, s3):
+        assert abs(a - b) <= 1e-15 * b
+
+
+def test_oracle_reproduces_2x4_example(ex2x4):
+    """Scores equal to the example rows: q = e_0, k_j = x_j e_0, scale 1, V = I."""
+    inp = np.asarray(ex2x4["inp"], dtype=np.float32)
+    for r in range(2):
+        q = np.eye(4, dtype=np.float32)[0].reshape(1, 1, 1, 4)
+        k = np.zeros((1, 1, 4, 4), np.float32)
+        k[0, 0, :, 0] = inp[r]
+        v = np.eye(4, dtype=np.float32).reshape(1, 1, 4, 4)
+        O, lse = oracle.attention(q, k, v, 1.0)
+        expect_p = np.exp(inp[r].astype(np.float64) - ex2x4["xmax"][r]) / ex2x4["xsum"][r]
+        assert_close(O.reshape(4), expect_p, 1e-15, "softmax row")
+        assert abs(lse.item() - ex2x4["lse"][r]) <= 1e-14
+
+
+# ----------------------------------------------------------------------------
+# CANN FA post: online softmax (corrected reading) == two-pass softmax_standard
+# ----------------------------------------------------------------------------
+def softmax_standard_weighted(x, vals):
+    m = max(x)
+    e = [math.exp(xi - m) for xi in x]
+    tot = sum(e)
+    return sum(ei * vi for ei, vi in zip(e, vals)) / tot
+
+
+def softmax_online_weighted(x, vals):
+    """running (m, l, o): both l and o are rescaled by exp(m - m_new); O = o / l."""
+    m, l, o = -math.inf, 0.0, 0.0
+    for xi, vi in zip(x, vals):
+        m_new = max(m, xi)
+        c = math.exp(m - m_new)
+        l = l * c + math.exp(xi - m_new)
+        o = o * c + math.exp(xi - m_new) * vi
+        m = m_new
+    return o / l
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64])
+def test_online_equals_two_pass(n):
+    for _ in range(20):
+        x = (RNG.standard_normal(n) * 4).tolist()
+        vals = RNG.standard_normal(n).tolist()
+        a = softmax_online_weighted(x, vals)
+        b = softmax_standard_weighted(x, vals)
+        assert abs(a - b) <= 1e-13 * max(1.0, abs(b))
+
+
+def test_printed_online_listing_is_garbled():
+    """The printed listing multiplies o by the already-updated l; that reading is
+    not the softmax-weighted sum, the corrected one is."""
+    x = [0.0, 1.0, 2.0]
+    vals = [1.0, 2.0, 3.0]
+    m, l, o = -math.inf, 0.0, 0.0
+    for xi, vi in zip(x, vals):
+        m_new = max(m, xi)
+        l = l * math.exp(m - m_new) + math.exp(xi - m_new)
+        o = o * l * math.exp(m - m_new) + math.exp(xi - m_new) * vi
+        m = m_new
+    good = softmax_standard_weighted(x, vals)
+    assert abs(o - good) > 0.1
+    assert abs(softmax_online_weighted(x, vals) - good) <= 1e-14
+
+
+# ----------------------------------------------------------------------------
+# invariants of the definition
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_rows_sum_to_one(causal):
+    L = 24
+    q, k = rnd(2, 3, L, L), rnd(2, 3, L, L)
+    v = np.broadcast_to(np.eye(L, dtype=np.float32), (2, 3, L, L)).copy()
+    O, _ = oracle.attention(q, k, v, 0.37, causal)
+    assert np.all(O >= 0.0)
+    assert np.max(np.abs(O.sum(-1) - 1.0)) <= 1e-14
+    if causal:
+        upper = np.triu(np.ones((L, L), bool), 1)
+        assert np.all(O[..., upper] == 0.0)
+
+
+def test_constant_v_gives_constant_o():
+    q, k = rnd(1, 4, 33, 8, scale=3), rnd(1, 2, 40, 8, scale=3)
+    v = np.full((1, 2, 40, 8), -1.75, np.float32)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625], np.float32)
+    for kw in ({}, {"alibi_slopes": slopes}, {"bias": rnd(4, 33, 40)}):
+        for causal in (False, True):
+            O, lse = oracle.attention(q, k, v, 0.5, causal, **kw)
+            assert np.max(np.abs(O + 1.75)) <= 1e-14
+            assert np.all(np.isfinite(lse))
+
+
+def test_constant_bias_shifts_lse_only():
+    q, k, v = rnd(2, 2, 9, 8), rnd(2, 2, 13, 8), rnd(2, 2, 13, 8)
+    O0, l0 = oracle.attention(q, k, v, 0.4, True)
+    O1, l1 = oracle.attention(q, k, v, 0.4, True, bias=np.full((1,), 2.5, np.float32))
+    assert_close(O1, O0, 1e-14, "O")
+    assert_close(l1, l0 + 2.5, 1e-13, "LSE")
+
+
+def test_two_keys_exact_weights():
+    """q = 0 so every score is its bias; bias (0, ln 3) gives weights (1/4, 3/4)."""
+    q = np.zeros((1, 1, 1, 4), np.float32)
+    k = rnd(1, 1, 2, 4)
+    v = np.array([[1, 0, 2, 0], [0, 1, 2, 4]], np.float32).reshape(1, 1, 2, 4)
+    bias = np.array([0.0, math.log(3.0)], np.float32).reshape(1, 1, 1, 2)
+    O, lse = oracle.attention(q, k, v, 1.0, bias=bias)
+    b1 = float(np.float32(math.log(3.0)))
+    w1 = math.exp(b1) / (1 + math.exp(b1))
+    v64 = v.astype(np.float64)
+    expect = (1 - w1) * v64[0, 0, 0] + w1 * v64[0, 0, 1]
+    assert_close(O.reshape(4), expect, 1e-15, "O")
+    assert abs(lse.item() - math.log(1 + math.exp(b1))) <= 1e-15
+    assert abs(w1 - 0.75) < 1e-7
+
+
+@pytest.mark.parametrize("Lq,Lk", [(16, 16), (5, 12), (1, 30)])
+def test_zero_q_gives_mean_of_visible(Lq, Lk):
+    q = np.zeros((1, 2, Lq, 8), np.float32)
+    k, v = rnd(1, 2, Lk, 8), rnd(1, 2, Lk, 8)
+    O, lse = oracle.attention(q, k, v, 0.9, True)
+    for i in range(Lq):
+        n = i + (Lk - Lq) + 1
+        assert_close(O[0, :, i], v[0, :, :n].astype(np.float64).mean(1), 1e-14, "mean")
+        assert np.max(np.abs(lse[0, :, i] - math.log(n))) <= 1e-14
+
+
+def test_causal_row0_is_v0():
+    q, k, v = rnd(2, 3, 10, 16), rnd(2, 3, 10, 16), rnd(2, 3, 10, 16)
+    O, lse = oracle.attention(q, k, v, 0.25, True)
+    assert_close(O[:, :, 0], v[:, :, 0].astype(np.float64), 1e-15, "O_0")
+    s00 = 0.25 * np.einsum("bhd,bhd->bh", q[:, :, 0].astype(np.float64), k[:, :, 0].astype(np.float64))
+    assert_close(lse[:, :, 0], s00, 1e-14, "LSE_0")
+
+
+def test_decode_query_sees_all_keys():
+    q, k, v = rnd(3, 4, 1, 16), rnd(3, 2, 50, 16), rnd(3, 2, 50, 16)
+    a = oracle.attention(q, k, v, 0.25, True)
+    b = oracle.attention(q, k, v, 0.25, False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_fully_masked_rows():
+    """Lq > Lk with causal alignment to the end: the first Lq - Lk rows see nothing."""
+    q, k, v = rnd(1, 2, 8, 4), rnd(1, 2, 5, 4), rnd(1, 2, 5, 4)
+    O, lse = oracle.attention(q, k, v, 1.0, True)
+    assert np.all(O[:, :, :3] == 0.0)
+    assert np.all(np.isneginf(lse[:, :, :3]))
+    assert np.all(np.isfinite(lse[:, :, 3:]))
+    Ob, lb = brute(q, k, v, 1.0, True)
+    assert_close(O, Ob, 1e-14, "O")
+    assert_close(lse, lb, 1e-13, "LSE")
+
+
+def test_empty_key_set():
+    q = rnd(1, 1, 3, 4)
+    k = np.zeros((1, 1, 0, 4), np.float32)
+    O, lse = oracle.attention(q, k, k, 1.0)
+    assert np.all(O == 0.0) and np.all(np.isneginf(lse))
+
+
+# ----------------------------------------------------------------------------
+# brute force through scipy
+# ----------------------------------------------------------------------------
+BRUTE_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, scale, causal, bias
+    (1, 1, 1, 16, 16, 8, 0.35, False, None),
+    (2, 2, 2, 17, 17, 16, 0.25, True, None),
+    (1, 4, 2, 9, 31, 8, 0.5, True, None),
+    (2, 8, 2, 1, 64, 16, 0.125, False, None),
+    (1, 6, 3, 33, 20, 4, 1.0, True, "dense"),
+    (2, 4, 4, 20, 45, 8, 0.3, True, "alibi"),
+    (1, 4, 1, 64, 64, 64, 0.125, False, "alibi"),
+    (2, 2, 1, 12, 12, 1, 2.0, False, "dense_b"),
+]
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES, ids=[str(i) for i in range(len(BRUTE_CASES))])
+def test_brute_force(case):
+    B, Hq, Hkv, Lq, Lk, D, scale, causal, bias_kind = case
+    q, k, v = rnd(B, Hq, Lq, D, scale=2), rnd(B, Hkv, Lk, D, scale=2), rnd(B, Hkv, Lk, D)
+    kw, bkw = {}, {}
+    if bias_kind == "dense":
+        bias = rnd(Hq, Lq, Lk)
+        kw["bias"] = bias
+        bkw["bias"] = bias[None]
+    elif bias_kind == "dense_b":
+        bias = rnd(B, 1, Lq, Lk)
+        kw["bias"] = bias
+        bkw["bias"] = bias
+    elif bias_kind == "alibi":
+        slopes = np.power(2.0, -8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        kw["alibi_slopes"] = slopes
+        bkw["slopes"] = slopes
+    O, lse = oracle.attention(q, k, v, scale, causal, **kw)
+    Ob, lb = brute(q, k, v, scale, causal, **bkw)
+    assert_close(O, Ob, 1e-12, "O")
+    assert_close(lse, lb, 1e-12, "LSE")
+
+
+def test_gqa_equals_repeated_mha():
+    q, k, v = rnd(2, 8, 11, 16), rnd(2, 2, 19, 16), rnd(2, 2, 19, 16)
+    a = oracle.attention(q, k, v, 0.3, True)
+    b = oracle.attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), 0.3, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = oracle.attention(q, np.tile(k, (1, 4, 1, 1)), np.tile(v, (1, 4, 1, 1)), 0.3, True)
+    assert np.max(np.abs(c[0] - a[0])) > 1e-2
+
+
+def test_alibi_zero_slopes_is_no_bias():
+    q, k, v = rnd(1, 4, 10, 8), rnd(1, 4, 14, 8), rnd(1, 4, 14, 8)
+    a = oracle.attention(q, k, v, 0.5, True, alibi_slopes=np.zeros(4, np.float32))
+    b = oracle.attention(q, k, v, 0.5, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_alibi_equals_dense_formula():
+    Hq, Lq, Lk = 4, 10, 14
+    q, k, v = rnd(1, Hq, Lq, 8), rnd(1, Hq, Lk, 8), rnd(1, Hq, Lk, 8)
+    slopes = np.power(2.0, -8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+    pos = np.arange(Lq)[:, None] + (Lk - Lq)
+    dense = (-slopes.astype(np.float64)[:, None, None] * np.abs(pos - np.arange(Lk)[None, :]))
+    for causal in (False, True):
+        a = oracle.attention(q, k, v, 0.5, causal, alibi_slopes=slopes)
+        b = oracle.attention(q, k, v, 0.5, causal, bias=dense.astype(np.float32))
+        assert_close(a[0], b[0], 1e-14, "O")
+        assert_close(a[1], b[1], 1e-13, "LSE")
+
+
+def test_large_logits_stay_finite():
+    """q and K scaled by 40 (Mirage lecture section 5.5): logits in the
+    thousands; an unstabilised exp overflows, the stable definition does not."""
+    q, k, v = rnd(1, 2, 16, 8, scale=40), rnd(1, 2, 32, 8, scale=40), rnd(1, 2, 32, 8)
+    O, lse = oracle.attention(q, k, v, 1.0, False)
+    S = np.einsum("bhid,bhjd->bhij", q.astype(np.float64), k.astype(np.float64))
+    assert np.max(np.abs(S)) > 700
+    with np.errstate(over="ignore", invalid="ignore"):
+        naive = np.exp(S).sum(-1)
+    assert not np.all(np.isfinite(naive))
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
+    Ob, lb = brute(q, k, v, 1.0, False)
+    assert_close(O, Ob, 1e-12, "O")
+    assert np.max(np.abs(lse - lb)) <= 1e-12 * np.max(np.abs(lb))
+
+
+def test_row_subset_and_thread_count():
+    q, k, v = rnd(2, 4, 21, 16), rnd(2, 2, 21, 16), rnd(2, 2, 21, 16)
+    O, lse = oracle.attention(q, k, v, 0.25, True, threads=1)
+    O8, lse8 = oracle.attention(q, k, v, 0.25, True, threads=8)
+    assert np.array_equal(O, O8) and np.array_equal(lse, lse8)
+    rows = [0, 5, 83, 2 * 4 * 21 - 1, 40]
+    Os, ls = oracle.attention(q, k, v, 0.25, True, rows=rows)
+    assert np.array_equal(Os, O.reshape(-1, 16)[rows])
+    assert np.array_equal(ls, lse.reshape(-1)[rows])
+
+
+# ----------------------------------------------------------------------------
+# split-K combine
+# ----------------------------------------------------------------------------
+def partials_from_oracle(q, k, v, scale, bounds, shift_rng=None, lib=None):
+    """(o_s, m_s, l_s) per chunk from the oracle on each key chunk:
+    o_s = O_s, m_s = LSE_s, l_s = 1, optionally re-referenced to m_s + delta_s."""
+    os_, ms, ls = [], [], []
+    for a, b in bounds:
+        O, lse = oracle.attention(q, k[:, :, a:b], v[:, :, a:b], scale, False, lib=lib)
+        l = np.ones_like(lse)
+        if shift_rng is not None:
+            delta = shift_rng.uniform(-3, 3, size=lse.shape)
+            fin = np.isfinite(lse)
+            l = np.where(fin, np.exp(-delta), 0.0)
+            O = O * np.where(fin, np.exp(-delta), 0.0)[..., None]
+            lse = np.where(fin, lse + delta, lse)
+        else:
+            O = np.where(np.isfinite(lse)[..., None], O, 0.0)
+            l = np.where(np.isfinite(lse), l, 0.0)
+        os_.append(O)
+        ms.append(lse)
+        ls.append(l)
+    return np.stack(os_, -2), np.stack(ms, -1), np.stack(ls, -1)
+
+
+@pytest.mark.parametrize("bounds", [
+    [(0, 128)],
+    [(0, 64), (64, 128)],
+    [(0, 32), (32, 64), (64, 96), (96, 128)],
+    [(4 * s, 4 * s + 4) for s in range(32)],
+    [(0, 50), (50, 51), (51, 128)],
+    [(0, 70), (70, 70), (70, 128), (128, 128)],
+])
+def test_combine_equals_unsplit(bounds):
+    q, k, v = rnd(2, 4, 1, 16, scale=2), rnd(2, 2, 128, 16, scale=2), rnd(2, 2, 128, 16)
+    O, lse = oracle.attention(q, k, v, 0.3, False)
+    for shift in (None, np.random.default_rng(7)):
+        op, mp, lp = partials_from_oracle(q, k, v, 0.3, bounds, shift)
+        Oc, lc = oracle.splitk_combine(op, mp, lp)
+        assert_close(Oc, O, 1e-6, "O")   # partials pass through fp32
+        assert_close(lc, lse, 1e-6, "LSE")
+
+
+def test_combine_four_chunks_small_head():
+    """1 query, 32 keys, head dim 8, four KV chunks (Mirage lecture section 5.5)."""
+    q, k, v = rnd(1, 1, 1, 8), rnd(1, 1, 32, 8), rnd(1, 1, 32, 8)
+    O, lse = oracle.attention(q, k, v, 1.0)
+    op, mp, lp = partials_from_oracle(q, k, v, 1.0, [(8 * s, 8 * s + 8) for s in range(4)],
+                                      np.random.default_rng(3))
+    Oc, lc = oracle.splitk_combine(op, mp, lp)
+    assert_close(Oc, O, 1e-6, "O")
+    assert_close(lc, lse, 1e-6, "LSE")
+
+
+def test_combine_all_empty_row():
+    op = np.zeros((2, 3, 4), np.float32)
+    mp = np.full((2, 3), -np.inf, np.float32)
+    lp = np.zeros((2, 3), np.float32)
+    Oc, lc = oracle.splitk_combine(op, mp, lp)
+    assert np.all(Oc == 0.0) and np.all(np.isneginf(lc))
+
+
+def test_combine_exact_weights():
+    """Two chunks with m = (0, ln 3), l = 1: weights 1/4 and 3/4, LSE = ln 4."""
+    op = np.array([[[4.0, 0.0], [0.0, 4.0]]], np.float32)
+    mp = np.array([[0.0, math.log(3.0)]], np.float32)
+    lp = np.ones((1, 2), np.float32)
+    Oc, lc = oracle.splitk_combine(op, mp, lp)
+    m1 = float(np.float32(math.log(3.0)))
+    w1 = math.exp(m1) / (1 + math.exp(m1))
+    assert_close(Oc.reshape(2), np.array([4 * (1 - w1), 4 * w1]), 1e-15, "O")
+    assert abs(lc.item() - math.log(1 + math.exp(m1))) <= 1e-15
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes must be caught
+# ----------------------------------------------------------------------------
+MUTANTS = {
+    "kv_head_modulo": ("const int64_t hk = h / G;", "const int64_t hk = h % J->Hkv;"),
+    "dropped_scale": ("double sj = J->scale * dot;", "double sj = dot;"),
+    "alibi_sign": ("sj += -(double)J->slopes[h] * dist;", "sj += (double)J->slopes[h] * dist;"),
+    "causal_off_by_one": ("nvis = p + 1;", "nvis = p;"),
+    "causal_top_left": ("const int64_t p = i + (J->Lk - J->Lq);", "const int64_t p = i;"),
+    "lse_log2": ("*lse = m + log(l);", "*lse = m + log2(l);"),
+    "missing_normalise": ("for (int64_t d = 0; d < D; ++d) o[d] /= l;", ";"),
+    "combine_weight_sign": ("const double w = exp(ms - M);", "const double w = exp(M - ms);"),
+    "combine_unscaled_l": ("L += w * (double)l_part[r * S + s];", "L += (double)l_part[r * S + s];"),
+    "dense_bias_transposed": ("sj += (double)J->bias[b * st[0] + h * st[1] + i * st[2] + j * st[3]];",
+                              "sj += (double)J->bias[b * st[0] + h * st[1] + j * st[2] + i * st[3]];"),
+}
+
+
+def _pin_suite(lib):
+    """A compact run of the pins above against library ``lib``; True if all pass."""
+    try:
+        for case in BRUTE_CASES:
+            B, Hq, Hkv, Lq, Lk, D, scale, causal, bias_kind = case
+            rng = np.random.default_rng(11)
+            q = rng.standard_normal((B, Hq, Lq, D)).astype(np.float32)
+            k = rng.standard_normal((B, Hkv, Lk, D)).astype(np.float32)
+            v = rng.standard_normal((B, Hkv, Lk, D)).astype(np.float32)
+            kw, bkw = {}, {}
+            if bias_kind in ("dense", "dense_b"):
+                bias = rng.standard_normal((B, Hq, Lq, Lk)).astype(np.float32)
+                kw["bias"] = bkw["bias"] = bias
+            elif bias_kind == "alibi":
+                slopes = np.power(2.0, -8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+                kw["alibi_slopes"] = bkw["slopes"] = slopes
+            O, lse = oracle.attention(q, k, v, scale, causal, lib=lib, **kw)
+            Ob, lb = brute(q, k, v, scale, causal, **bkw)
+            assert_close(O, Ob, 1e-12, "O")
+            assert_close(lse, lb, 1e-12, "LSE")
+        rng = np.random.default_rng(5)
+        q = rng.standard_normal((1, 2, 1, 8)).astype(np.float32)
+        k = rng.standard_normal((1, 2, 64, 8)).astype(np.float32)
+        v = rng.standard_normal((1, 2, 64, 8)).astype(np.float32)
+        O, lse = brute(q, k, v, 0.5)
+        op, mp, lp = partials_from_oracle(q, k, v, 0.5, [(0, 20), (20, 64)], rng, lib=lib)
+        Oc, lc = oracle.splitk_combine(op, mp, lp, lib=lib)
+        assert_close(Oc, O, 1e-6, "combine O")
+        assert_close(lc, lse, 1e-6, "combine LSE")
+    except AssertionError:
+        return False
+    return True
+
+
+def test_pin_suite_accepts_oracle():
+    assert _pin_suite(oracle.load())
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_planted_mistake(name, tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, "mutation anchor not found: " + name
+    path = tmp_path / ("mut_%s.c" % name)
+    path.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / ("libmut_%s.so" % name))
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-o", lib_path,
+                    str(path), "-lm"], check=True)
+    assert not _pin_suite(oracle.load_path(lib_path)), "planted mistake not caught: " + name
