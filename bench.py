@@ -1,0 +1,306 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+Default run (N = 1):
+  * prefill leg -- the causal bf16 workload B=4, H=32, L=4096, d=128; one step
+    is one attn_fwd_prefill call over inputs already resident in HBM.  `value`
+    is its throughput in algorithmic TFLOP/s (4 * d FLOP per visible
+    query/key pair, masked pairs not counted).
+  * decode leg -- the split-K GQA workload B=16, Hq=32, Hkv=8, Lk=32768,
+    d=128, 32 chunks of 1024 keys; one step is the local split-K kernel
+    followed by the combine.  Reported under "decode" in algorithmic GB/s.
+  * roofline -- for the dominant kernel of each leg, algorithmic work per
+    launch / the average launch duration measured with HIP events on the
+    stream the kernel runs on.
+  * cpu_baseline -- the fp64 oracle, timed on the host cores on a bounded
+    sample of the prefill workload (whole heads), scaled to TFLOP/s.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
+METRIC = "prefill TFLOP/s (% MFMA peak); decode HBM GB/s (% of peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (shared with the tests that pin these formulas)
+# ----------------------------------------------------------------------------
+def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
+    """(query, key) pairs that enter the softmax for one head."""
+    if not causal:
+        return Lq * Lk
+    off = Lk - Lq
+    total = 0
+    # row i sees min(Lk, max(0, i + off + 1)) keys
+    first_full = max(0, Lk - off - 1)          # rows i >= first_full see all Lk keys
+    lo = max(0, -off)                          # rows below lo see nothing
+    hi = min(Lq, first_full)
+    if hi > lo:
+        n = hi - lo
+        a = lo + off + 1
+        total += n * a + n * (n - 1) // 2
+    if Lq > max(hi, lo):
+        total += (Lq - max(hi, lo)) * Lk
+    return total
+
+
+def attention_flops(B, Hq, Lq, Lk, D, causal) -> int:
+    """2*D FLOP for q.k and 2*D for p*v per visible pair."""
+    return 4 * D * B * Hq * visible_pairs(Lq, Lk, causal)
+
+
+def prefill_bytes(B, Hq, Hkv, Lq, Lk, D, elem=2, o_elem=2) -> int:
+    """Q, K, V read once; O and LSE written once."""
+    return (B * Hq * Lq * D + 2 * B * Hkv * Lk * D) * elem + B * Hq * Lq * D * o_elem + B * Hq * Lq * 4
+
+
+def decode_partial_kernel_bytes(B, Hq, Hkv, Lq, Lk, D, S, elem=2) -> int:
+    """local split-K step: Q and K/V read once, partials (o, m, l) written once."""
+    return (B * Hq * Lq * D + 2 * B * Hkv * Lk * D) * elem + B * Hq * Lq * S * (D + 2) * 4
+
+
+def decode_step_bytes(B, Hq, Hkv, Lq, Lk, D, S, elem=2, o_elem=2) -> int:
+    """whole decode: the local step, the partials read back, O and LSE written."""
+    return (decode_partial_kernel_bytes(B, Hq, Hkv, Lq, Lk, D, S, elem) + B * Hq * Lq * S * (D + 2) * 4
+            + B * Hq * Lq * D * o_elem + B * Hq * Lq * 4)
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["online_softmax_fusion_amd/csrc/prefill_bf16.hip", "online_softmax_fusion_amd/csrc/attn_device.h"]
+DECODE_SOURCES = ["online_softmax_fusion_amd/csrc/decode_bf16.hip", "online_softmax_fusion_amd/csrc/attn_device.h"]
+
+
+def measured_traffic(kernel: str, workload: str, sources) -> "int | None":
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = table.get(kernel)
+    if not ent or ent.get("workload") != workload or ent.get("source_digest") != source_digest(sources):
+        return None
+    return int(ent["traffic_bytes"])
+
+
+# ----------------------------------------------------------------------------
+# legs
+# ----------------------------------------------------------------------------
+def time_prefill(w, steps, warmup):
+    import torch
+    import synth
+    import online_softmax_fusion_amd as attn
+
+    log("prefill leg: %s, generating inputs" % w.name)
+    q, k, v = synth.make_qkv(w, device="cuda")
+    kw = {}
+    if w.bias == "alibi":
+        kw["alibi_slopes"] = synth.alibi_slopes(w.Hq).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
+    scale = w.softmax_scale()
+    for _ in range(warmup):
+        attn.attn_fwd_prefill(q, k, v, scale, w.causal, out=o, lse=lse, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        attn.attn_fwd_prefill(q, k, v, scale, w.causal, out=o, lse=lse, **kw)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_ms = sum(durs) / len(durs)
+    flops = attention_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+    log("prefill: wall %.3f ms/step, kernel avg %.4f ms (p10 %.4f, p90 %.4f)" %
+        (wall * 1e3 / steps, avg_ms, durs[len(durs) // 10], durs[(9 * len(durs)) // 10]))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return wall / steps, avg_ms * 1e-3, flops, durs
+
+
+def time_decode(w, steps, warmup):
+    import torch
+    import synth
+    import online_softmax_fusion_amd as attn
+
+    log("decode leg: %s, generating inputs" % w.name)
+    q, k, v = synth.make_qkv(w, device="cuda")
+    S = w.splits or attn.attn_decode_choose_splits(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, attn.attn_device_cu_count(0))
+    kv_bytes = 2 * k.numel() * k.element_size()
+    copies = max(1, math.ceil((512 << 20) / kv_bytes))     # keep the working set past the 256 MB cache
+    kvs = [(k, v)] + [(k.clone(), v.clone()) for _ in range(copies - 1)]
+    if copies > 1:
+        log("decode: rotating %d K/V copies (%.0f MiB each)" % (copies, kv_bytes / 2 ** 20))
+    op = torch.empty((w.B, w.Hq, w.Lq, S, w.D), dtype=torch.float32, device="cuda")
+    mp = torch.empty((w.B, w.Hq, w.Lq, S), dtype=torch.float32, device="cuda")
+    lp = torch.empty_like(mp)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
+    scale = w.softmax_scale()
+
+    def step(i, evs=None):
+        kk, vv = kvs[i % copies]
+        if evs:
+            evs[0].record(stream)
+        attn.attn_fwd_decode_splitk(q, kk, vv, S, scale, w.causal, o_part=op, m_part=mp, l_part=lp)
+        if evs:
+            evs[1].record(stream)
+        attn.attn_splitk_combine(op, mp, lp, out=o, lse=lse)
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_ms = sum(durs) / len(durs)
+    log("decode: S=%d, wall %.4f ms/step, partial kernel avg %.4f ms" % (S, wall * 1e3 / steps, avg_ms))
+    del q, k, v, kvs, op, mp, lp, o, lse
+    torch.cuda.empty_cache()
+    return wall / steps, avg_ms * 1e-3, S
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle as it stands, on whole heads of the prefill workload."""
+    import numpy as np
+    import synth
+    import oracle
+
+    threads = oracle.default_threads()
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        threads = max(1, min(threads, int(env)))
+    G = w.Hq // w.Hkv
+
+    def run(n_heads):
+        ws = w.with_(B=1, Hq=n_heads * G, Hkv=n_heads)   # n K/V heads with their query groups
+        q, k, v = synth.make_qkv(ws)
+        q, k, v = q.float().numpy(), k.float().numpy(), v.float().numpy()
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, w.softmax_scale(), w.causal, threads=threads)
+        t = time.perf_counter() - t0
+        return t, attention_flops(1, n_heads * G, w.Lq, w.Lk, w.D, w.causal)
+
+    t1, f1 = run(1)
+    n = int(max(1, min(w.B * w.Hkv, round(budget_s / max(t1, 1e-3)))))
+    if n > 1:
+        t1, f1 = run(n)
+    log("cpu baseline: %d head(s) in %.2f s on %d threads" % (n, t1, threads))
+    return {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole K/V head(s) with their %d query head(s) each (%d query rows x %d keys%s, "
+                      "d=%d), drawn with the workload's recipe, of %s; fp64; %.1f s" %
+                      (n, G, w.Lq, w.Lk, ", causal" if w.causal else "", w.D, w.name, t1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill", default=None, help="prefill workload name (default: causal B4 H32 L4096)")
+    ap.add_argument("--decode", default=None, help="decode workload name (default: GQA B16 Lk32768)")
+    ap.add_argument("--splits", type=int, default=None, help="override the decode split count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requested %d)" %
+              max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("steps must be >= 1 and warmup >= 0")
+
+    import torch
+    import synth
+    import online_softmax_fusion_amd as attn
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    attn.load_library()
+    wp = synth.WORKLOADS[args.prefill] if args.prefill else synth.C2_CAUSAL
+    wd = synth.WORKLOADS[args.decode] if args.decode else synth.C4_DECODE
+    if args.splits:
+        wd = wd.with_(splits=args.splits)
+
+    torch.cuda.synchronize()
+    step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup)
+    d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup)
+
+    p_tflops = flops / step_s / 1e12
+    p_kern_tflops = flops / kern_s / 1e12
+    d_bytes = decode_step_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S)
+    d_kern_bytes = decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S)
+    d_gbs = d_bytes / d_step_s / 1e9
+    d_kern_gbs = d_kern_bytes / d_kern_s / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs)",
+        "config": {"workload": wp.name, "B": wp.B, "H": wp.Hq, "Lq": wp.Lq, "Lk": wp.Lk, "D": wp.D,
+                   "causal": wp.causal, "bias": wp.bias, "parallelism": "single GPU"},
+        "roofline": {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": round(p_kern_tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(p_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill_bf16_kernel", wp.name, PREFILL_SOURCES)},
+        "decode": {"workload": wd.name, "splits": S, "value": round(d_gbs, 1), "unit": "GB/s",
+                   "ms_per_step": round(d_step_s * 1e3, 4),
+                   "roofline": {"kernel": "decode_bf16_kernel", "bound": "hbm", "achieved": round(d_kern_gbs, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_kern_gbs / HBM_PEAK_GBS, 4),
+                                "traffic": measured_traffic("decode_bf16_kernel", wd.name, DECODE_SOURCES)}},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wp, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention forward library
+ * (libattn_mi355x.so).
+ *
+ * The operation is the attention chain of "Neptune论文浅读：把FlashAttention式融合
+ * 放进编译器" (gentlecold.top), section 2: S = scale * Q K^T, then the score
+ * modifier (causal mask, additive bias), then the stable softmax of each score
+ * row, then P V.  It is computed in one pass over the keys without writing the
+ * Lq x Lk score matrix anywhere:
+ *   - prefill uses the rolling update of section 5 of those notes (running
+ *     max m and sum l per query row, the accumulated sum and output repaired by
+ *     exp(m_old - m_new) whenever the max grows, section 3 and section 4);
+ *   - decode uses the split-K update of section 6: the keys are cut into
+ *     chunks, each chunk yields a local (o, m, l), and a global step repairs
+ *     the chunks with the global max and merges them.
+ * The variants covered are those listed in section 9 of the notes that change
+ * the score only: global (no mask), causal, ALiBi, dense additive bias, and GQA
+ * (query heads sharing K/V heads, CMU 15-779 Lecture 11 "Mirage" notes,
+ * section 7.1), in prefill and decode form.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *   Layout       Q [B, Hq, Lq, D]; K, V [B, Hkv, Lk, D]; O [B, Hq, Lq, D]; the
+ *                last dimension (d) is contiguous, the b, h, l strides are given
+ *                in ELEMENTS.  LSE [B, Hq, Lq] is contiguous fp32.
+ *   GQA          Hq % Hkv == 0; query head h reads K/V head h / (Hq / Hkv)
+ *                (contiguous groups of query heads share one K/V head).
+ *   Score        s_ij = scale * <q_i, k_j> + bias_ij (bias is not scaled).
+ *   Causal       aligned to the end of the keys: key j is visible to query row
+ *                i iff j <= i + (Lk - Lq).  For Lq == Lk this is the lower
+ *                triangle; a single decode query (Lq = 1) sees every key.
+ *   ALiBi        bias_ij = -alibi_slopes[h] * |i + (Lk - Lq) - j|.
+ *   Output       O_i = sum_j softmax(s_i)_j v_j;  LSE_i = ln sum_j exp(s_ij)
+ *                (natural log).  A row with no visible key gets O_i = 0 and
+ *                LSE_i = -inf (never NaN).
+ *   Arithmetic   bf16 inputs are multiplied on the matrix cores with fp32
+ *                accumulation; the softmax, the running max/sum, LSE and all
+ *                partials are fp32.  fp32 inputs are computed in fp32.
+ *   Pointers     every tensor pointer is a DEVICE pointer owned by the caller;
+ *                the library never allocates, frees or synchronises, keeps no
+ *                state except a per-device cache of the compute-unit count, and
+ *                enqueues its kernels on the given HIP stream (a hipStream_t
+ *                passed as void*, NULL = the null stream).  Calls return as soon
+ *                as the kernels are enqueued.  Calls are thread-safe.
+ *   Alignment    q, k, v and o base pointers must be 16-byte aligned and every
+ *                b/h/l stride a multiple of 16 bytes' worth of elements.
+ *   Errors       arguments are checked on the host before anything is
+ *                enqueued; a failed check returns ATTN_ERR_INVALID_ARG (bad
+ *                value) or ATTN_ERR_UNSUPPORTED (valid but not implemented:
+ *                D not in {64, 128}, dtype combination, alignment) and enqueues
+ *                nothing.  A launch failure returns ATTN_ERR_HIP.  No C++
+ *                exception crosses this interface.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,
+    ATTN_ERR_UNSUPPORTED = 2,
+    ATTN_ERR_WORKSPACE = 3,
+    ATTN_ERR_HIP = 4
+} attn_status;
+
+/* Element types (values of the *_dtype fields). */
+enum { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Score-bias kinds (values of bias_kind). */
+enum { ATTN_BIAS_NONE = 0, ATTN_BIAS_DENSE = 1, ATTN_BIAS_ALIBI = 2 };
+
+/*
+ * Arguments of one attention forward problem (the problem statement of the
+ * Neptune notes, section 2: Q, K, V, scale, mask, bias; section 9: the causal,
+ * ALiBi and GQA variants).
+ */
+typedef struct attn_fwd_args {
+    int64_t B, Hq, Hkv, Lq, Lk, D;   /* batch, query heads, K/V heads, query rows, keys, head dim */
+    int32_t dtype;                   /* ATTN_F32 or ATTN_BF16: element type of q, k and v */
+    int32_t causal;                  /* 0 = every key visible; 1 = end-aligned causal mask */
+    const void *q, *k, *v;           /* device pointers */
+    int64_t q_strides[3];            /* b, h, l strides of q in elements (d stride is 1) */
+    int64_t k_strides[3];
+    int64_t v_strides[3];
+    float scale;                     /* multiplies <q, k> before the bias is added */
+    int32_t bias_kind;               /* ATTN_BIAS_NONE / ATTN_BIAS_DENSE / ATTN_BIAS_ALIBI */
+    const void *bias;                /* DENSE: device pointer to the bias, element (b,h,i,j) at
+                                        b*bias_strides[0] + h*bias_strides[1] + i*bias_strides[2]
+                                        + j*bias_strides[3]; a stride of 0 broadcasts */
+    int32_t bias_dtype;              /* ATTN_F32 or ATTN_BF16 */
+    int32_t o_dtype;                 /* ATTN_F32 or ATTN_BF16: element type of o */
+    int64_t bias_strides[4];
+    const float *alibi_slopes;       /* ALIBI: device pointer to Hq fp32 slopes */
+    void *o;                         /* device pointer, O [B, Hq, Lq, D] */
+    int64_t o_strides[3];            /* b, h, l strides of o in elements */
+    float *lse;                      /* device pointer to [B, Hq, Lq] fp32, or NULL */
+} attn_fwd_args;
+
+/*
+ * attn_fwd_prefill -- fused attention forward with the rolling update
+ * (Neptune notes, section 5; the loop structure of the CANN FlashAttention
+ * post: a query tile stays on chip while K/V tiles stream past it).
+ * Writes o and, when lse != NULL, lse.  Any Lq, Lk >= 0.
+ */
+attn_status attn_fwd_prefill(const attn_fwd_args *a, void *stream);
+
+/*
+ * attn_fwd_decode_splitk -- local step of the split-K update (Neptune notes,
+ * section 6).  The keys are cut into num_splits chunks
+ *     chunk s = [s*C, min((s+1)*C, Lk)),  C = 32 * ceil(Lk / (32 * num_splits)),
+ * and for every query row (b, h, i) and chunk s it writes, in fp32,
+ *     m_part[b,h,i,s]   a reference value (natural-log units) for the chunk,
+ *     l_part[b,h,i,s] = sum_j exp(s_ij - m),
+ *     o_part[b,h,i,s,:] = sum_j exp(s_ij - m) v_j      (not normalised),
+ * over the visible keys j of the chunk.  A chunk with no visible key gives
+ * m = -inf, l = 0, o = 0.  The query heads of one K/V group are processed
+ * together so each K/V element is read once per group (Mirage lecture notes,
+ * section 7.1).  o_part is [B, Hq, Lq, num_splits, D] and m_part, l_part are
+ * [B, Hq, Lq, num_splits], all contiguous device fp32 buffers owned by the
+ * caller (attn_decode_partial_bytes gives their total size).  a->o and a->lse
+ * are not used.  Any Lq >= 0 (Lq = 1 is the decode case), 1 <= num_splits <= 65535.
+ */
+attn_status attn_fwd_decode_splitk(const attn_fwd_args *a, int32_t num_splits,
+                                   float *o_part, float *m_part, float *l_part, void *stream);
+
+/*
+ * attn_splitk_combine -- global step of the split-K update (Neptune notes,
+ * section 6, with the repair term exp(r - r') of section 4): for every row,
+ *     M = max_s m_s,  w_s = exp(m_s - M),  L = sum_s w_s l_s,
+ *     O = sum_s w_s o_s / L,  LSE = M + ln L;
+ * a row whose chunks are all empty gets O = 0, LSE = -inf.  The partials are
+ * laid out as attn_fwd_decode_splitk writes them (rows = B*Hq*Lq).  o is
+ * [B, Hq, Lq, D] with the given strides and element type; lse may be NULL.
+ */
+attn_status attn_splitk_combine(const float *o_part, const float *m_part, const float *l_part,
+                                int64_t B, int64_t Hq, int64_t Lq, int64_t D, int32_t num_splits,
+                                void *o, int32_t o_dtype, const int64_t o_strides[3],
+                                float *lse, void *stream);
+
+/*
+ * attn_decode_choose_splits -- split count for attn_fwd_decode_splitk (pure
+ * host function, no HIP call).  Picks the number of key chunks so that the
+ * B * Hkv * ceil(Lq*Hq/Hkv / 32) * num_splits workgroups fill cu_count compute
+ * units several times over while keeping at least 256 keys per chunk (an
+ * under-filled grid is what the Mirage lecture notes, section 7.1, measure as
+ * the cost of fixed grid heuristics).  Returns >= 1; 1 when Lk <= 256.
+ */
+int32_t attn_decode_choose_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                                  int32_t cu_count);
+
+/* attn_decode_partial_bytes -- bytes of o_part + m_part + l_part for a decode call. */
+size_t attn_decode_partial_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int32_t num_splits);
+
+/* attn_device_cu_count -- compute units of HIP device `device` (cached); <= 0 on error. */
+int32_t attn_device_cu_count(int32_t device);
+
+/*
+ * attn_validate_prefill / attn_validate_decode -- the host-side argument
+ * check that the corresponding entry point runs before enqueuing anything
+ * (pure host functions, no HIP call; usable without a GPU).
+ */
+attn_status attn_validate_prefill(const attn_fwd_args *a);
+attn_status attn_validate_decode(const attn_fwd_args *a, int32_t num_splits,
+                                 const float *o_part, const float *m_part, const float *l_part);
+
+/* attn_fwd_args_size -- sizeof(attn_fwd_args), so a binding can check its mirror of the struct. */
+size_t attn_fwd_args_size(void);
+
+/* attn_status_str -- static English text for a status code. */
+const char *attn_status_str(attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,302 @@
+"""Python binding of the MI355X fused attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn_mi355x.so`` behind the C ABI of ``include/attn.h``.
+PyTorch supplies device memory and the current HIP stream.  There is no CPU
+or PyTorch fallback: if the library is missing, loading fails loudly.
+
+Entry points (same names as the C ABI):
+    attn_fwd_prefill(q, k, v, ...)             -> (o, lse)
+    attn_fwd_decode_splitk(q, k, v, splits, ...) -> (o_part, m_part, l_part)
+    attn_splitk_combine(o_part, m_part, l_part, ...) -> (o, lse)
+and the conveniences ``prefill`` (= attn_fwd_prefill) and ``decode`` (split-K
+local step followed by the combine on the same stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "AttnError", "load_library", "library_path", "attn_fwd_prefill", "attn_fwd_decode_splitk",
+    "attn_splitk_combine", "attn_decode_choose_splits", "attn_decode_partial_bytes",
+    "attn_device_cu_count", "prefill", "decode", "chunk_length", "AttnFwdArgs",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn_mi355x.so")
+_LIB = None
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, 1, 2, 3, 4
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_BIAS_NONE, ATTN_BIAS_DENSE, ATTN_BIAS_ALIBI = 0, 1, 2
+
+_I64x3 = ctypes.c_int64 * 3
+_I64x4 = ctypes.c_int64 * 4
+
+
+class AttnFwdArgs(ctypes.Structure):
+    """Mirror of ``attn_fwd_args`` in include/attn.h (field order and types)."""
+    _fields_ = [
+        ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("Lq", ctypes.c_int64), ("Lk", ctypes.c_int64), ("D", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_strides", _I64x3), ("k_strides", _I64x3), ("v_strides", _I64x3),
+        ("scale", ctypes.c_float), ("bias_kind", ctypes.c_int32),
+        ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+        ("bias_strides", _I64x4), ("alibi_slopes", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("o_strides", _I64x3), ("lse", ctypes.c_void_p),
+    ]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = load_library()
+        msg = lib.attn_status_str(status).decode()
+        super().__init__("%s failed: %s (status %d)" % (what, msg, status))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libattn_mi355x.so; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libattn_mi355x.so is not built (run __graft_entry__.build() or "
+                          "python online_softmax_fusion_amd/build.py); there is no fallback path")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(AttnFwdArgs)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.attn_fwd_prefill.argtypes = [P, vp]
+    lib.attn_fwd_prefill.restype = ctypes.c_int
+    lib.attn_fwd_decode_splitk.argtypes = [P, i32, vp, vp, vp, vp]
+    lib.attn_fwd_decode_splitk.restype = ctypes.c_int
+    lib.attn_splitk_combine.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, vp, i32,
+                                        ctypes.POINTER(ctypes.c_int64), vp, vp]
+    lib.attn_splitk_combine.restype = ctypes.c_int
+    lib.attn_decode_choose_splits.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.attn_decode_choose_splits.restype = i32
+    lib.attn_decode_partial_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_decode_partial_bytes.restype = ctypes.c_size_t
+    lib.attn_device_cu_count.argtypes = [i32]
+    lib.attn_device_cu_count.restype = i32
+    lib.attn_validate_prefill.argtypes = [P]
+    lib.attn_validate_prefill.restype = ctypes.c_int
+    lib.attn_validate_decode.argtypes = [P, i32, vp, vp, vp]
+    lib.attn_validate_decode.restype = ctypes.c_int
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_fwd_args_size.argtypes = []
+    lib.attn_fwd_args_size.restype = ctypes.c_size_t
+    if lib.attn_fwd_args_size() != ctypes.sizeof(AttnFwdArgs):
+        raise ImportError("attn_fwd_args layout mismatch between include/attn.h and the binding")
+    _LIB = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return ATTN_BF16
+    if t == torch.float32:
+        return ATTN_F32
+    raise TypeError("only bfloat16 and float32 tensors are supported, got %s" % t)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check_4d(name: str, t: torch.Tensor):
+    if t.dim() != 4:
+        raise ValueError("%s must be 4-D [B, H, L, D], got shape %s" % (name, tuple(t.shape)))
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("%s must have a contiguous last dimension" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _strides3(t: torch.Tensor):
+    return _I64x3(*[int(x) for x in t.stride()[:3]])
+
+
+def _make_args(q, k, v, scale, causal, bias, alibi_slopes, o=None, lse=None) -> AttnFwdArgs:
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_4d(name, t)
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    if tuple(v.shape) != (Bk, Hkv, Lk, Dk) or Bk != B or Dk != D:
+        raise ValueError("shape mismatch: q %s, k %s, v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    a = AttnFwdArgs()
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.D = B, Hq, Hkv, Lq, Lk, D
+    a.dtype = _dtype_code(q.dtype)
+    a.causal = 1 if causal else 0
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.q_strides, a.k_strides, a.v_strides = _strides3(q), _strides3(k), _strides3(v)
+    a.scale = float(scale) if scale is not None else 1.0 / math.sqrt(D)
+    a.bias_kind = ATTN_BIAS_NONE
+    a.bias_dtype = ATTN_F32
+    if bias is not None and alibi_slopes is not None:
+        raise ValueError("give either a dense bias or ALiBi slopes, not both")
+    if bias is not None:
+        if not bias.is_cuda:
+            raise ValueError("bias must be a GPU tensor")
+        bb = bias
+        while bb.dim() < 4:
+            bb = bb.unsqueeze(0)
+        bb = bb.expand(B, Hq, Lq, Lk)
+        a.bias_kind = ATTN_BIAS_DENSE
+        a.bias = bb.data_ptr()
+        a.bias_dtype = _dtype_code(bb.dtype)
+        a.bias_strides = _I64x4(*[int(x) for x in bb.stride()])
+    elif alibi_slopes is not None:
+        if not alibi_slopes.is_cuda or alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq:
+            raise ValueError("alibi_slopes must be a GPU fp32 tensor with one slope per query head")
+        a.bias_kind = ATTN_BIAS_ALIBI
+        a.alibi_slopes = alibi_slopes.contiguous().data_ptr()
+    if o is not None:
+        a.o = _ptr(o)
+        a.o_dtype = _dtype_code(o.dtype)
+        a.o_strides = _strides3(o)
+    else:
+        a.o_dtype = a.dtype
+    a.lse = _ptr(lse)
+    return a
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+def attn_fwd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                     causal: bool = False, *, bias: Optional[torch.Tensor] = None,
+                     alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused attention forward (rolling update).  q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D].
+
+    Returns (O [B,Hq,Lq,D], LSE [B,Hq,Lq] fp32 or None).  ``bias`` broadcasts to
+    [B,Hq,Lq,Lk]; ``alibi_slopes`` is an fp32 [Hq] tensor.
+    """
+    lib = load_library()
+    B, Hq, Lq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _check_4d("out", out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq * Lq):
+        raise ValueError("lse must be a contiguous fp32 tensor of B*Hq*Lq elements")
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, out, lse)
+    st = lib.attn_fwd_prefill(ctypes.byref(a), _stream(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_prefill")
+    return out, lse
+
+
+prefill = attn_fwd_prefill
+
+
+def chunk_length(Lk: int, num_splits: int) -> int:
+    """Keys per split-K chunk: 32 * ceil(Lk / (32 * num_splits)) (include/attn.h)."""
+    per = -(-Lk // (32 * num_splits))
+    return 32 * max(per, 1)
+
+
+def attn_fwd_decode_splitk(q, k, v, num_splits: int, scale: Optional[float] = None, causal: bool = False, *,
+                           bias=None, alibi_slopes=None, o_part=None, m_part=None, l_part=None):
+    """Split-K local step: partials (o [B,Hq,Lq,S,D], m [B,Hq,Lq,S], l [B,Hq,Lq,S]) in fp32."""
+    lib = load_library()
+    B, Hq, Lq, D = q.shape
+    S = int(num_splits)
+    dev = q.device
+    if o_part is None:
+        o_part = torch.empty((B, Hq, Lq, S, D), dtype=torch.float32, device=dev)
+    if m_part is None:
+        m_part = torch.empty((B, Hq, Lq, S), dtype=torch.float32, device=dev)
+    if l_part is None:
+        l_part = torch.empty((B, Hq, Lq, S), dtype=torch.float32, device=dev)
+    for name, t, n in (("o_part", o_part, B * Hq * Lq * S * D), ("m_part", m_part, B * Hq * Lq * S),
+                       ("l_part", l_part, B * Hq * Lq * S)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n or not t.is_cuda:
+            raise ValueError("%s must be a contiguous GPU fp32 tensor of %d elements" % (name, n))
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes)
+    st = lib.attn_fwd_decode_splitk(ctypes.byref(a), S, _ptr(o_part), _ptr(m_part), _ptr(l_part), _stream(dev))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_decode_splitk")
+    return o_part, m_part, l_part
+
+
+def attn_splitk_combine(o_part, m_part, l_part, *, out=None, out_dtype=torch.bfloat16, lse=None,
+                        return_lse: bool = True):
+    """Split-K global step: (O [B,Hq,Lq,D], LSE [B,Hq,Lq]) from the partials."""
+    lib = load_library()
+    if o_part.dim() != 5:
+        raise ValueError("o_part must be [B, Hq, Lq, S, D]")
+    B, Hq, Lq, S, D = o_part.shape
+    for name, t in (("o_part", o_part), ("m_part", m_part), ("l_part", l_part)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous GPU fp32 tensor" % name)
+    if tuple(m_part.shape) != (B, Hq, Lq, S) or tuple(l_part.shape) != (B, Hq, Lq, S):
+        raise ValueError("m_part and l_part must be [B, Hq, Lq, S]")
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=out_dtype, device=o_part.device)
+    else:
+        _check_4d("out", out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=o_part.device)
+    st = lib.attn_splitk_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), B, Hq, Lq, D, S, _ptr(out),
+                                 _dtype_code(out.dtype), _strides3(out), _ptr(lse), _stream(o_part.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_splitk_combine")
+    return out, lse
+
+
+def attn_decode_choose_splits(B: int, Hq: int, Hkv: int, Lq: int, Lk: int, cu_count: int = 0) -> int:
+    return int(load_library().attn_decode_choose_splits(B, Hq, Hkv, Lq, Lk, cu_count))
+
+
+def attn_decode_partial_bytes(B: int, Hq: int, Lq: int, D: int, num_splits: int) -> int:
+    return int(load_library().attn_decode_partial_bytes(B, Hq, Lq, D, num_splits))
+
+
+def attn_device_cu_count(device: int = 0) -> int:
+    return int(load_library().attn_device_cu_count(device))
+
+
+def decode(q, k, v, num_splits: Optional[int] = None, scale: Optional[float] = None, causal: bool = False, *,
+           bias=None, alibi_slopes=None, out=None, out_dtype=None, workspace=None, return_lse: bool = True):
+    """Split-K decode: local step then combine, both enqueued on the current stream.
+
+    ``workspace`` may be a tuple (o_part, m_part, l_part) to reuse.
+    """
+    B, Hq, Lq, D = q.shape
+    if num_splits is None:
+        cu = attn_device_cu_count(q.device.index or 0)
+        num_splits = attn_decode_choose_splits(B, Hq, k.shape[1], Lq, k.shape[2], cu)
+    o_part = m_part = l_part = None
+    if workspace is not None:
+        o_part, m_part, l_part = workspace
+    o_part, m_part, l_part = attn_fwd_decode_splitk(q, k, v, num_splits, scale, causal, bias=bias,
+                                                    alibi_slopes=alibi_slopes, o_part=o_part,
+                                                    m_part=m_part, l_part=l_part)
+    return attn_splitk_combine(o_part, m_part, l_part, out=out, out_dtype=out_dtype or q.dtype,
+                               return_lse=return_lse)

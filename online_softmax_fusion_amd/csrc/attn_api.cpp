@@ -1,0 +1,230 @@
+// attn_api.cpp -- the C ABI of include/attn.h: argument checks on the host,
+// choice of kernel instantiation, and launches on the caller's stream.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_kernels.h"
+
+using attn::FwdParams;
+
+namespace {
+
+constexpr int64_t kIntMax = 0x7fffffff;
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+int64_t elem_size(int32_t dt) { return dt == ATTN_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t dt) { return dt == ATTN_F32 || dt == ATTN_BF16; }
+
+// Checks shared by prefill and decode.
+attn_status check_common(const attn_fwd_args *a) {
+    if (a == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (a->B < 0 || a->Hq < 1 || a->Hkv < 1 || a->Lq < 0 || a->Lk < 0 || a->D < 1)
+        return ATTN_ERR_INVALID_ARG;
+    if (a->Hq % a->Hkv != 0) return ATTN_ERR_INVALID_ARG;
+    if (!valid_dtype(a->dtype)) return ATTN_ERR_INVALID_ARG;
+    if (a->causal != 0 && a->causal != 1) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(a->scale)) return ATTN_ERR_INVALID_ARG;
+    for (int t = 0; t < 3; ++t)
+        if (a->q_strides[t] < 0 || a->k_strides[t] < 0 || a->v_strides[t] < 0) return ATTN_ERR_INVALID_ARG;
+    if (a->bias_kind != ATTN_BIAS_NONE && a->bias_kind != ATTN_BIAS_DENSE && a->bias_kind != ATTN_BIAS_ALIBI)
+        return ATTN_ERR_INVALID_ARG;
+
+    const int64_t rows = a->B * a->Hq * a->Lq;
+    const bool any_q = rows > 0;
+    const bool any_kv = a->B * a->Hkv * a->Lk > 0;
+    if (any_q && a->q == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (any_q && any_kv && (a->k == nullptr || a->v == nullptr)) return ATTN_ERR_INVALID_ARG;
+    if (a->bias_kind == ATTN_BIAS_DENSE) {
+        if (any_q && any_kv && a->bias == nullptr) return ATTN_ERR_INVALID_ARG;
+        if (!valid_dtype(a->bias_dtype)) return ATTN_ERR_INVALID_ARG;
+        for (int t = 0; t < 4; ++t)
+            if (a->bias_strides[t] < 0) return ATTN_ERR_INVALID_ARG;
+        if (!aligned(a->bias, (uintptr_t)elem_size(a->bias_dtype))) return ATTN_ERR_UNSUPPORTED;
+    }
+    if (a->bias_kind == ATTN_BIAS_ALIBI && any_q && a->alibi_slopes == nullptr) return ATTN_ERR_INVALID_ARG;
+
+    // implemented shapes
+    if (a->D != 64 && a->D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (a->Lq > kIntMax / 2 || a->Lk > kIntMax / 2 || a->B * a->Hq > kIntMax || rows > kIntMax)
+        return ATTN_ERR_UNSUPPORTED;
+    // 16-byte vector loads of q, k, v rows
+    const int64_t vec = 16 / elem_size(a->dtype);
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16)) return ATTN_ERR_UNSUPPORTED;
+    for (int t = 0; t < 3; ++t)
+        if (a->q_strides[t] % vec || a->k_strides[t] % vec || a->v_strides[t] % vec) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+FwdParams make_params(const attn_fwd_args *a) {
+    FwdParams p{};
+    p.q = a->q; p.k = a->k; p.v = a->v;
+    p.q_sb = a->q_strides[0]; p.q_sh = a->q_strides[1]; p.q_sl = a->q_strides[2];
+    p.k_sb = a->k_strides[0]; p.k_sh = a->k_strides[1]; p.k_sl = a->k_strides[2];
+    p.v_sb = a->v_strides[0]; p.v_sh = a->v_strides[1]; p.v_sl = a->v_strides[2];
+    p.o = a->o;
+    p.o_sb = a->o_strides[0]; p.o_sh = a->o_strides[1]; p.o_sl = a->o_strides[2];
+    p.o_bf16 = a->o_dtype == ATTN_BF16;
+    p.lse = a->lse;
+    p.B = (int)a->B; p.Hq = (int)a->Hq; p.Hkv = (int)a->Hkv; p.G = (int)(a->Hq / a->Hkv);
+    p.Lq = (int)a->Lq; p.Lk = (int)a->Lk; p.D = (int)a->D;
+    p.causal = a->causal;
+    p.scale = a->scale;
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    p.bias = a->bias;
+    p.bias_sb = a->bias_strides[0]; p.bias_sh = a->bias_strides[1];
+    p.bias_si = a->bias_strides[2]; p.bias_sj = a->bias_strides[3];
+    p.slopes = a->alibi_slopes;
+    if (a->bias_kind == ATTN_BIAS_ALIBI)
+        p.bias_kind = attn::kBiasAlibi;
+    else if (a->bias_kind == ATTN_BIAS_DENSE)
+        p.bias_kind = a->bias_dtype == ATTN_BF16 ? attn::kBiasDenseBf16 : attn::kBiasDenseF32;
+    else
+        p.bias_kind = attn::kBiasNone;
+    return p;
+}
+
+int32_t chunk_len(int64_t Lk, int32_t S) {
+    const int64_t per = (Lk + (int64_t)S * 32 - 1) / ((int64_t)S * 32);
+    return (int32_t)(per < 1 ? 32 : per * 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_validate_prefill(const attn_fwd_args *a) {
+    attn_status st = check_common(a);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(a->o_dtype)) return ATTN_ERR_INVALID_ARG;
+    for (int t = 0; t < 3; ++t)
+        if (a->o_strides[t] < 0) return ATTN_ERR_INVALID_ARG;
+    if (a->B * a->Hq * a->Lq > 0) {
+        if (a->o == nullptr) return ATTN_ERR_INVALID_ARG;
+        const int64_t vec = 16 / elem_size(a->o_dtype);
+        if (!aligned(a->o, 16)) return ATTN_ERR_UNSUPPORTED;
+        for (int t = 0; t < 3; ++t)
+            if (a->o_strides[t] % vec) return ATTN_ERR_UNSUPPORTED;
+        if (a->lse != nullptr && !aligned(a->lse, 4)) return ATTN_ERR_INVALID_ARG;
+    }
+    return ATTN_OK;
+}
+
+attn_status attn_validate_decode(const attn_fwd_args *a, int32_t num_splits, const float *o_part,
+                                 const float *m_part, const float *l_part) {
+    attn_status st = check_common(a);
+    if (st != ATTN_OK) return st;
+    if (num_splits < 1 || num_splits > 65535) return ATTN_ERR_INVALID_ARG;
+    if (a->B * a->Hq * a->Lq > 0) {
+        if (o_part == nullptr || m_part == nullptr || l_part == nullptr) return ATTN_ERR_INVALID_ARG;
+        if (!aligned(o_part, 16) || !aligned(m_part, 4) || !aligned(l_part, 4)) return ATTN_ERR_INVALID_ARG;
+    }
+    const int64_t G = a->Hq / a->Hkv;
+    if (a->B * a->Hkv > 65535 || (G * a->Lq + 31) / 32 > 65535) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+attn_status attn_fwd_prefill(const attn_fwd_args *a, void *stream) {
+    attn_status st = attn_validate_prefill(a);
+    if (st != ATTN_OK) return st;
+    if (a->B * a->Hq * a->Lq == 0) return ATTN_OK;
+    FwdParams p = make_params(a);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = (a->dtype == ATTN_BF16) ? attn::launch_prefill_bf16(p, s) : attn::launch_rows_f32(p, 0, s);
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd_decode_splitk(const attn_fwd_args *a, int32_t num_splits, float *o_part, float *m_part,
+                                   float *l_part, void *stream) {
+    attn_status st = attn_validate_decode(a, num_splits, o_part, m_part, l_part);
+    if (st != ATTN_OK) return st;
+    if (a->B * a->Hq * a->Lq == 0) return ATTN_OK;
+    FwdParams p = make_params(a);
+    p.num_splits = num_splits;
+    p.chunk = chunk_len(a->Lk, num_splits);
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = (a->dtype == ATTN_BF16) ? attn::launch_decode_bf16(p, s) : attn::launch_rows_f32(p, 1, s);
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_splitk_combine(const float *o_part, const float *m_part, const float *l_part, int64_t B,
+                                int64_t Hq, int64_t Lq, int64_t D, int32_t num_splits, void *o, int32_t o_dtype,
+                                const int64_t o_strides[3], float *lse, void *stream) {
+    if (B < 0 || Hq < 1 || Lq < 0 || D < 1 || num_splits < 1 || num_splits > 65535) return ATTN_ERR_INVALID_ARG;
+    if (!valid_dtype(o_dtype) || o_strides == nullptr) return ATTN_ERR_INVALID_ARG;
+    for (int t = 0; t < 3; ++t)
+        if (o_strides[t] < 0) return ATTN_ERR_INVALID_ARG;
+    const int64_t rows = B * Hq * Lq;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (rows > kIntMax / 4) return ATTN_ERR_UNSUPPORTED;
+    if (rows == 0) return ATTN_OK;
+    if (o_part == nullptr || m_part == nullptr || l_part == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(o_part, 4) || !aligned(m_part, 4) || !aligned(l_part, 4) || !aligned(o, (uintptr_t)elem_size(o_dtype)))
+        return ATTN_ERR_INVALID_ARG;
+    if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+    attn::CombineParams c{};
+    c.o_part = o_part; c.m_part = m_part; c.l_part = l_part;
+    c.o = o; c.o_sb = o_strides[0]; c.o_sh = o_strides[1]; c.o_sl = o_strides[2];
+    c.lse = lse;
+    c.B = (int)B; c.Hq = (int)Hq; c.Lq = (int)Lq; c.D = (int)D; c.S = num_splits;
+    c.o_bf16 = o_dtype == ATTN_BF16;
+    hipError_t err = attn::launch_combine(c, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int32_t attn_decode_choose_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int32_t cu_count) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Hq % Hkv != 0 || Lk <= 256) return 1;
+    const int64_t cu = cu_count > 0 ? cu_count : 256;
+    const int64_t rblocks = ((Hq / Hkv) * Lq + 31) / 32;
+    const int64_t units = B * Hkv * rblocks;
+    const int64_t target = 2 * cu;               // two resident workgroups per compute unit
+    int64_t S = (target + units - 1) / units;
+    const int64_t max_by_len = Lk / 256;         // at least 256 keys per chunk
+    if (S > max_by_len) S = max_by_len;
+    if (S > 65535) S = 65535;
+    if (S < 1) S = 1;
+    return (int32_t)S;
+}
+
+size_t attn_decode_partial_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int32_t num_splits) {
+    if (B < 0 || Hq < 0 || Lq < 0 || D < 0 || num_splits < 1) return 0;
+    const size_t rows = (size_t)B * (size_t)Hq * (size_t)Lq * (size_t)num_splits;
+    return rows * (size_t)D * sizeof(float) + 2 * rows * sizeof(float);
+}
+
+int32_t attn_device_cu_count(int32_t device) {
+    static std::atomic<int32_t> cache[64];
+    if (device < 0) return -1;
+    if (device < 64) {
+        const int32_t c = cache[device].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return -1;
+    if (device < 64) cache[device].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+size_t attn_fwd_args_size(void) { return sizeof(attn_fwd_args); }
+
+const char *attn_status_str(attn_status s) {
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID_ARG: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_WORKSPACE: return "workspace too small";
+        case ATTN_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// attn_device.h -- device-side helpers shared by the gfx950 attention kernels.
+//
+// Everything here is CDNA4 (gfx950) specific: wave64, the 32x32x16 bf16 matrix
+// core instruction, v_exp_f32 (2^x), v_cvt_pk_bf16_f32 and v_permlane32_swap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+// D += A * B on the matrix core, 32x32 output, k = 16, bf16 operands, fp32
+// accumulate.  Lane l supplies row (l % 32) of A and column (l % 32) of B, each
+// as 8 consecutive k values starting at 8 * (l / 32); accumulator element
+// 4*i + j of lane l is row 8*i + 4*(l/32) + j, column l % 32.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of x held by lane (l ^ 32), using the cross-half swap of gfx950.
+// Returns {x[l], x[l^32]} in some order; callers only use symmetric
+// combinations (max, sum) of the pair.
+__device__ __forceinline__ float xor32_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Two floats to a packed pair of bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 load16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void store16(void *p, const u32x4 &v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// Swap bits 2 and 3 of a row index inside a 32-row block.  Loading key
+// perm32(r) into matrix-core row r makes the accumulator of S^T = K Q^T hold,
+// in lane l, keys 8*(l/32) + 0..7 in elements 0..7 and 16 + 8*(l/32) + 0..7 in
+// elements 8..15 -- exactly the B-operand layout the P V product needs, so P
+// never leaves registers.  The map is its own inverse.
+__device__ __forceinline__ int perm32(int r) {
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+}  // namespace attn

@@ -1,0 +1,66 @@
+"""The algorithmic FLOP and byte counts used by bench.py, pinned to the numbers
+printed in the CMU 15-779 Lecture 11 (Mirage) notes -- section 1.2 / section 10
+(one head, N=4096, d=128, bf16) and section 12 exercise 6 (GQA decode traffic)
+-- and to brute-force counts of the causal mask."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import bench
+import synth
+
+
+@pytest.fixture(scope="module")
+def numbers(golden_dir):
+    with open(os.path.join(golden_dir, "roofline_numbers.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 5), (7, 12), (12, 7), (1, 9), (9, 1), (64, 64), (0, 5), (5, 0)])
+def test_visible_pairs_brute(Lq, Lk):
+    pos = np.arange(Lq)[:, None] + (Lk - Lq)
+    brute = int(np.sum(np.arange(Lk)[None, :] <= pos)) if Lq and Lk else 0
+    assert bench.visible_pairs(Lq, Lk, True) == brute
+    assert bench.visible_pairs(Lq, Lk, False) == Lq * Lk
+
+
+def test_head_matmul_flops(numbers):
+    h = numbers["head"]
+    f = bench.attention_flops(1, 1, h["N"], h["N"], h["d"], False)
+    assert abs(f / 1e9 - h["matmul_GFLOP"]) < 0.05
+
+
+def test_head_traffic(numbers):
+    h = numbers["head"]
+    N, d, e = h["N"], h["d"], h["bytes_per_elem"]
+    nxn = 2 * N * N * e                                  # write once, read once
+    flash = bench.prefill_bytes(1, 1, 1, N, N, d, e, e) - N * 4   # Q, K, V in, O out (no LSE)
+    assert round(nxn / 1e6) == h["nxn_write_plus_read_MB"]
+    assert abs(flash / 1e6 - h["flash_total_MB"]) < 0.05
+    assert round((nxn + flash) / 1e6) == h["graph_level_total_MB"]
+    assert round((nxn + flash) / flash) == h["reduction_factor"]
+
+
+def test_gqa_exercise(numbers):
+    g = numbers["gqa"]
+    kv = 2 * g["batch"] * g["kv_heads"] * g["context"] * g["d"] * g["bytes_per_elem"]
+    assert round(kv / 1e6) == g["kv_MB"]
+    per_q = kv * g["q_heads_per_group"]
+    assert round(per_q / 1e6) == g["per_query_head_MB"]
+    assert round(per_q / (g["bandwidth_TBps"] * 1e12) * 1e6) == g["per_query_head_us"]
+    assert round(kv / (g["bandwidth_TBps"] * 1e12) * 1e6) == g["grouped_us"]
+    # our decode byte count reads each K/V element once per group, like the grouped form
+    Hq = g["kv_heads"] * g["q_heads_per_group"]
+    step = bench.decode_partial_kernel_bytes(g["batch"], Hq, g["kv_heads"], 1, g["context"], g["d"], 1)
+    assert step - kv == g["batch"] * Hq * g["d"] * 2 + g["batch"] * Hq * (g["d"] + 2) * 4
+
+
+def test_workload_counts():
+    w = synth.C2_CAUSAL
+    assert bench.attention_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, True) == 549_890_031_616
+    w = synth.C5_PREFILL
+    assert round(bench.attention_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, True) / 1e9, 2) == 2199.09
+    w = synth.C4_DECODE
+    assert bench.decode_step_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, 32) == 2_164_787_200

@@ -1,0 +1,95 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times, on sampled output rows that the fp64 oracle computes one by one (GPU).
+
+Inputs are drawn on the GPU with the seeded recipe of ``synth``; the oracle
+receives host copies of exactly the stored values of the heads it needs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import online_softmax_fusion_amd as attn
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, LSE_TOL = 1.5e-2, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    attn.load_library()
+
+
+def sample_rows(L, rng, n=10):
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, L // 2, L - 129, L - 128, L - 2, L - 1]
+    rnd = rng.integers(0, L, size=n).tolist()
+    return sorted({r for r in fixed + rnd if 0 <= r < L})
+
+
+def check_heads(w, q, k, v, o, lse, heads, rows, slopes=None):
+    """Compare rows of heads [(b, h), ...] against the oracle, per head."""
+    G = w.Hq // w.Hkv
+    worst_o = worst_l = 0.0
+    for b, h in heads:
+        hk = h // G
+        qh = q[b:b + 1, h:h + 1].float().cpu()
+        kh = k[b:b + 1, hk:hk + 1].float().cpu()
+        vh = v[b:b + 1, hk:hk + 1].float().cpu()
+        kw = {}
+        if slopes is not None:
+            kw["alibi_slopes"] = slopes[h:h + 1]
+        O_ref, L_ref = oracle.attention(qh, kh, vh, w.softmax_scale(), w.causal, rows=rows, **kw)
+        og = o[b, h, rows].float().cpu().numpy()
+        lg = lse[b, h, rows].cpu().numpy()
+        eo = float(np.max(np.abs(og - O_ref)))
+        el = float(np.max(np.abs(lg - L_ref)))
+        assert eo <= O_TOL, "%s b=%d h=%d: O err %.3e" % (w.name, b, h, eo)
+        assert el <= LSE_TOL, "%s b=%d h=%d: LSE err %.3e" % (w.name, b, h, el)
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    print("%s: worst O err %.3e, worst LSE err %.3e" % (w.name, worst_o, worst_l), flush=True)
+
+
+@pytest.mark.parametrize("w", [synth.C2_CAUSAL, synth.C3_ALIBI, synth.C5_PREFILL], ids=lambda w: w.name)
+def test_prefill_fullsize_sampled(w):
+    print("full-size prefill", w.name, flush=True)
+    rng = np.random.default_rng(w.seed)
+    q, k, v = synth.make_qkv(w, device="cuda")
+    slopes = synth.alibi_slopes(w.Hq) if w.bias == "alibi" else None
+    kw = {"alibi_slopes": slopes.cuda()} if slopes is not None else {}
+    o, lse = attn.attn_fwd_prefill(q, k, v, w.softmax_scale(), w.causal, **kw)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2)} |
+                   {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(2)})
+    check_heads(w, q, k, v, o, lse, heads, sample_rows(w.Lq, rng), slopes)
+
+
+@pytest.mark.parametrize("w", [synth.C4_DECODE, synth.C5_DECODE], ids=lambda w: w.name)
+def test_decode_fullsize(w):
+    print("full-size decode", w.name, flush=True)
+    q, k, v = synth.make_qkv(w, device="cuda")
+    S = w.splits or attn.attn_decode_choose_splits(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, attn.attn_device_cu_count(0))
+    o, lse = attn.decode(q, k, v, S, w.softmax_scale())
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(w.seed)
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    if len(heads) > 64:
+        idx = rng.choice(len(heads), size=64, replace=False)
+        heads = sorted(heads[i] for i in idx)
+    check_heads(w, q, k, v, o, lse, heads, [0])
+
+
+def test_tiny_reference_workload():
+    """The fp32 L=256, d=64 workload in full, 1e-5 on O and LSE."""
+    w = synth.C1_TINY
+    q, k, v = synth.make_qkv(w)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), w.causal)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), w.causal)
+    assert float(np.max(np.abs(o.cpu().double().numpy() - O_ref))) <= 1e-5
+    assert float(np.max(np.abs(lse.cpu().double().numpy() - L_ref))) <= 1e-5

@@ -1,0 +1,267 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs (GPU).
+
+Sizes span several query and key tiles with ragged tails.  Tolerances:
+  fp32 inputs: max |err| <= 1e-5 on O and LSE;
+  bf16 inputs (fp32 accumulation): max |err| <= 1.5e-2 on O, <= 1e-3 on LSE.
+Every call goes through the C ABI (the ctypes binding marshals arguments only).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import online_softmax_fusion_amd as attn
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (1.5e-2, 1e-3)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    attn.load_library()
+
+
+def compare(o_gpu, lse_gpu, O_ref, L_ref, dtype, what="", lse_tol=None):
+    o_tol, l_tol = TOL[dtype]
+    if lse_tol is not None:
+        l_tol = lse_tol
+    o = o_gpu.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o)), what + ": non-finite O"
+    err_o = float(np.max(np.abs(o - O_ref))) if o.size else 0.0
+    assert err_o <= o_tol, "%s: O max abs err %.3e > %.1e" % (what, err_o, o_tol)
+    if lse_gpu is not None:
+        l = lse_gpu.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(L_ref)
+        assert np.array_equal(np.isfinite(l), fin), what + ": LSE infinity pattern differs"
+        assert np.all(l[~fin] == -np.inf), what + ": masked rows must have LSE = -inf"
+        err_l = float(np.max(np.abs(l[fin] - L_ref[fin]))) if fin.any() else 0.0
+        assert err_l <= l_tol, "%s: LSE max abs err %.3e > %.1e" % (what, err_l, l_tol)
+    return err_o
+
+
+def inputs(B, Hq, Hkv, Lq, Lk, D, dtype, causal=False, bias="none", seed=1, qk_scale=1.0):
+    w = synth.Workload("case", B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, seed)
+    q, k, v = synth.make_qkv(w)
+    if qk_scale != 1.0:
+        q = (q.float() * qk_scale).to(q.dtype)
+        k = (k.float() * qk_scale).to(k.dtype)
+    gkw, okw = {}, {}
+    if bias == "alibi":
+        sl = synth.alibi_slopes(Hq)
+        gkw["alibi_slopes"], okw["alibi_slopes"] = sl.cuda(), sl
+    elif bias in ("dense_f32", "dense_bf16"):
+        bt = synth.make_dense_bias(w, (Hq, Lq, Lk), "f32" if bias == "dense_f32" else "bf16")
+        gkw["bias"], okw["bias"] = bt.cuda(), bt.float()
+    return w, q, k, v, gkw, okw
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias
+    (1, 1, 1, 256, 256, 64, "f32", False, "none"),        # tiny reference workload
+    (2, 3, 1, 150, 333, 128, "f32", True, "none"),
+    (1, 2, 2, 97, 200, 64, "f32", False, "alibi"),
+    (2, 4, 4, 300, 300, 128, "bf16", True, "none"),
+    (1, 4, 4, 200, 333, 128, "bf16", False, "none"),
+    (2, 4, 4, 260, 260, 64, "bf16", True, "none"),
+    (1, 8, 2, 190, 190, 128, "bf16", True, "none"),      # GQA
+    (1, 2, 2, 100, 450, 128, "bf16", True, "none"),      # Lq < Lk, end-aligned mask
+    (1, 2, 2, 300, 150, 128, "bf16", True, "none"),      # Lq > Lk: fully masked rows
+    (1, 4, 4, 257, 257, 128, "bf16", True, "alibi"),
+    (2, 2, 2, 130, 190, 128, "bf16", False, "alibi"),
+    (2, 2, 2, 96, 140, 128, "bf16", False, "dense_f32"),
+    (1, 2, 2, 129, 129, 64, "bf16", True, "dense_bf16"),
+    (1, 1, 1, 1, 77, 128, "bf16", False, "none"),
+    (1, 2, 1, 33, 1, 128, "bf16", True, "none"),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(i) for i in range(len(PREFILL_CASES))])
+def test_prefill_parity(case):
+    B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias = case
+    w, q, k, v, gkw, okw = inputs(B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, seed=17 + len(str(case)))
+    print("prefill case", case, flush=True)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), causal, **gkw)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, **okw)
+    compare(o, lse, O_ref, L_ref, dtype, str(case))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_fp32_output(dtype):
+    w, q, k, v, _, _ = inputs(1, 2, 2, 140, 140, 128, dtype, True)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), True,
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True)
+    err = compare(o, lse, O_ref, L_ref, dtype, "fp32 out")
+    if dtype == "bf16":
+        assert err <= 8e-3   # no final bf16 rounding of O
+
+
+def test_prefill_strided_views():
+    """q/k/v as views of a packed [B, L, 3, H, D] buffer (non-contiguous b/h/l strides)."""
+    B, H, L, D = 2, 4, 150, 128
+    w = synth.Workload("packed", B, H, H, L, L, D, "bf16", True, "none", 5)
+    packed = synth.normal((B, L, 3, H, D), 5, 0, "bf16")
+    q, k, v = (packed[:, :, t].permute(0, 2, 1, 3) for t in range(3))
+    g = packed.cuda()
+    qg, kg, vg = (g[:, :, t].permute(0, 2, 1, 3) for t in range(3))
+    o, lse = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), True)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True)
+    compare(o, lse, O_ref, L_ref, "bf16", "strided")
+
+
+def test_prefill_empty_keys():
+    q = synth.normal((1, 2, 40, 128), 3, 0, "bf16").cuda()
+    k = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = attn.attn_fwd_prefill(q, k, k, 0.1, False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_prefill_large_logits():
+    """q and K scaled by 40 (Mirage lecture notes, section 5.5): logits in the
+    thousands stay finite.  LSE is compared relative to its magnitude: the
+    fp32 score of a length-128 dot product of size ~1e4 carries ~1e-3 absolute
+    rounding; O and the relative LSE error keep the bf16 bars."""
+    w, q, k, v, _, _ = inputs(1, 2, 2, 130, 130, 128, "bf16", True, qk_scale=40.0, seed=9)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), True)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True)
+    assert np.max(np.abs(L_ref)) > 500
+    compare(o, lse, O_ref, L_ref, "bf16", "large logits",
+            lse_tol=1e-5 * float(np.max(np.abs(L_ref))) + 1e-3)
+
+
+def test_prefill_constant_v():
+    w, q, k, _, _, _ = inputs(1, 2, 2, 200, 200, 128, "bf16", True, seed=21)
+    v = torch.full(k.shape, 0.75, dtype=torch.bfloat16)
+    o, _ = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), True)
+    torch.cuda.synchronize()
+    assert float((o.float() - 0.75).abs().max()) <= 1.5e-2
+
+
+def test_prefill_deterministic():
+    w, q, k, v, _, _ = inputs(1, 4, 4, 300, 300, 128, "bf16", True, "alibi", seed=4)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    sl = synth.alibi_slopes(4).cuda()
+    a = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), True, alibi_slopes=sl)
+    b = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), True, alibi_slopes=sl)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------
+# split-K decode
+# ----------------------------------------------------------------------------
+DECODE_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, splits
+    (2, 8, 2, 1, 1000, 128, "bf16", False, "none", 3),
+    (2, 8, 2, 1, 1000, 128, "bf16", False, "none", 32),
+    (1, 4, 4, 1, 777, 128, "bf16", False, "none", 1),
+    (1, 4, 4, 1, 100, 128, "bf16", False, "none", 10),     # empty trailing chunks
+    (3, 32, 8, 1, 2048, 128, "bf16", False, "none", 4),
+    (1, 16, 2, 5, 700, 128, "bf16", True, "none", 6),       # 40 stacked rows: two row blocks
+    (1, 4, 1, 1, 999, 64, "bf16", False, "alibi", 5),
+    (2, 4, 2, 1, 300, 128, "bf16", False, "dense_f32", 3),
+    (1, 4, 2, 1, 500, 128, "f32", False, "none", 4),
+    (1, 2, 2, 3, 300, 64, "f32", True, "alibi", 2),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[str(i) for i in range(len(DECODE_CASES))])
+def test_decode_parity(case):
+    B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, S = case
+    w, q, k, v, gkw, okw = inputs(B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, seed=31 + S)
+    print("decode case", case, flush=True)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    op, mp, lp = attn.attn_fwd_decode_splitk(qg, kg, vg, S, w.softmax_scale(), causal, **gkw)
+    o, lse = attn.attn_splitk_combine(op, mp, lp, out_dtype=q.dtype)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, **okw)
+    compare(o, lse, O_ref, L_ref, dtype, "decode " + str(case))
+
+    # the combine kernel against the fp64 combine of the same partials
+    Oc, Lc = oracle.splitk_combine(op.cpu(), mp.cpu(), lp.cpu())
+    compare(attn.attn_splitk_combine(op, mp, lp, out_dtype=torch.float32)[0], lse, Oc, Lc, "f32",
+            "combine vs fp64 combine")
+
+    # each chunk's partial against the oracle restricted to that chunk
+    C = attn.chunk_length(Lk, S)
+    opc, mpc, lpc = op.cpu().double().numpy(), mp.cpu().double().numpy(), lp.cpu().double().numpy()
+    bias_t = okw.get("bias")
+    for s in range(S):
+        lo, hi = s * C, min((s + 1) * C, Lk)
+        if hi <= lo:
+            assert np.all(np.isneginf(mpc[..., s])) and np.all(lpc[..., s] == 0) and np.all(opc[..., s, :] == 0)
+            continue
+        # the chunk seen as its own attention problem: keep each row's position
+        # by shifting it with a dense mask equal to the original visibility
+        pos = np.arange(Lq)[:, None] + (Lk - Lq)
+        keys = np.arange(lo, hi)[None, :]
+        extra = np.zeros((Hq, Lq, hi - lo))
+        if causal:
+            extra = np.where(keys > pos, -np.inf, 0.0)[None].repeat(Hq, 0)
+        if "alibi_slopes" in okw:
+            sl = okw["alibi_slopes"].double().numpy()
+            extra = extra - sl[:, None, None] * np.abs(pos - keys)[None]
+        if bias_t is not None:
+            extra = extra + bias_t.double().numpy()[:, :, lo:hi]
+        Os, Ls = oracle.attention(q, k[:, :, lo:hi], v[:, :, lo:hi], w.softmax_scale(), False,
+                                  bias=extra.astype(np.float32))
+        l_s, m_s = lpc[..., s], mpc[..., s]
+        fin = np.isfinite(Ls)
+        assert np.array_equal(np.isfinite(m_s), fin)
+        got_lse = m_s[fin] + np.log(l_s[fin])
+        assert np.max(np.abs(got_lse - Ls[fin])) <= TOL[dtype][1], "chunk %d LSE" % s
+        got_o = opc[..., s, :][fin] / l_s[fin][:, None]
+        assert np.max(np.abs(got_o - Os[fin])) <= (1e-5 if dtype == "f32" else 1e-2), "chunk %d O" % s
+
+
+def test_decode_gqa_equals_repeated_heads():
+    w, q, k, v, _, _ = inputs(2, 8, 2, 1, 1500, 128, "bf16", seed=12)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    a = attn.decode(qg, kg, vg, 4, w.softmax_scale())
+    b = attn.decode(qg, kg.repeat_interleave(4, 1).contiguous(), vg.repeat_interleave(4, 1).contiguous(), 4,
+                    w.softmax_scale())
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 32])
+def test_decode_split_count_invariance(S):
+    """Split-K over any number of chunks equals the unsplit result (Neptune
+    notes section 6; Mirage lecture notes section 5.5, four chunks)."""
+    w, q, k, v, _, _ = inputs(1, 4, 4, 1, 1024, 128, "bf16", seed=40)
+    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), S, w.softmax_scale(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale())
+    compare(o, lse, O_ref, L_ref, "bf16", "S=%d" % S)
+
+
+def test_decode_deterministic():
+    w, q, k, v, _, _ = inputs(2, 8, 2, 1, 3000, 128, "bf16", seed=8)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    a = attn.decode(qg, kg, vg, 7, w.softmax_scale())
+    b = attn.decode(qg, kg, vg, 7, w.softmax_scale())
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_choose_splits_on_device():
+    cu = attn.attn_device_cu_count(0)
+    assert cu > 0
+    S = attn.attn_decode_choose_splits(1, 8, 8, 1, 32768, cu)
+    w, q, k, v, _, _ = inputs(1, 8, 8, 1, 4096, 128, "bf16", seed=2)
+    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), None, w.softmax_scale())
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale())
+    compare(o, lse, O_ref, L_ref, "bf16", "auto splits")
+    assert S >= 1
