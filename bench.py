@@ -237,6 +237,8 @@ def main():
     ap.add_argument("--splits", type=int, default=None, help="override the decode split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -253,6 +255,15 @@ def main():
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.copy_calibration:
+        n = 256 << 20
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 3}))
+        return
     attn.load_library()
     wp = synth.WORKLOADS[args.prefill] if args.prefill else synth.C2_CAUSAL
     wd = synth.WORKLOADS[args.decode] if args.decode else synth.C4_DECODE

@@ -59,6 +59,8 @@ attn_status check_common(const attn_fwd_args *a) {
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16)) return ATTN_ERR_UNSUPPORTED;
     for (int t = 0; t < 3; ++t)
         if (a->q_strides[t] % vec || a->k_strides[t] % vec || a->v_strides[t] % vec) return ATTN_ERR_UNSUPPORTED;
+    // key rows are addressed with 32-bit offsets inside a tile of keys
+    if (a->k_strides[2] > (1 << 24) || a->v_strides[2] > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
     return ATTN_OK;
 }
 

@@ -7,7 +7,8 @@
 
 namespace attn {
 
-enum BiasKind { kBiasNone = 0, kBiasAlibi = 1, kBiasDenseF32 = 2, kBiasDenseBf16 = 3 };
+// kBiasNoneScaled: no bias, score formed explicitly (used when the scale is not positive)
+enum BiasKind { kBiasNone = 0, kBiasAlibi = 1, kBiasDenseF32 = 2, kBiasDenseBf16 = 3, kBiasNoneScaled = 4 };
 
 // One attention problem after validation.  Strides are in elements.
 struct FwdParams {

@@ -11,9 +11,11 @@
 //      placed in the matrix-core rows with the perm32 shuffle so that each lane
 //      ends up holding 32 scores of ONE query row (its column), in exactly the
 //      order the P V product wants them.
-//   2. score modifier in the log2 domain: t = s * scale * log2(e) + bias *
-//      log2(e); the causal mask and the key tail are applied only on tiles that
-//      cross them.
+//   2. score modifier: without a bias the scale is folded into the exponent
+//      (one FMA per score: t = s * scale * log2(e) - m); with a bias the score
+//      is formed first, t = s * scale * log2(e) + bias * log2(e).  The causal
+//      mask and the key tail are applied only on tiles that cross them (a
+//      separate code path, so full tiles carry no compare at all).
 //   3. rolling update (Neptune notes section 3 and section 4): the row max
 //      over the tile needs one cross-half swap (v_permlane32_swap); when the
 //      max grows, the running sum and the output are repaired by
@@ -24,17 +26,22 @@
 //   4. P = 2^(t - m) in fp32; the row sum l accumulates the fp32 values (each
 //      lane keeps a partial over its half of the keys; the halves are added
 //      once at the end); P is packed to bf16 in registers.
-//   5. O^T += V^T P^T on the matrix cores, V^T read from LDS (V is transposed
-//      on its way into LDS), P^T straight from registers.  Each lane's output
-//      accumulators all belong to its own query row, so the repair in step 3
-//      is lane-local.
+//   5. O^T += V^T P^T on the matrix cores.  V stays in its natural [key][d]
+//      layout in LDS and the A operand (8 consecutive keys of one d per lane)
+//      is gathered with the transposing LDS read ds_read_b64_tr_b16; P^T comes
+//      straight from registers.  Each lane's output accumulators all belong to
+//      its own query row, so the repair in step 3 is lane-local.
 //
-// K/V tiles are double-buffered: the global loads for tile t+1 are issued
+// K/V tiles are double-buffered: the buffer loads for tile t+1 are issued
 // before the matrix work on tile t and written to the other LDS buffer after
 // it (the DMA/compute overlap described in the CANN post), one barrier per
-// tile.  Causal tiles above the diagonal are never loaded; a wave whose rows
-// are all above a tile's keys skips its matrix work.  Epilogue: O = O / l,
-// LSE = m ln 2 + ln l; a row with no visible key gets O = 0, LSE = -inf.
+// tile.  Buffer loads carry the key range in their descriptor, so rows past
+// the end of K/V read as zero without any branch.  Causal tiles above the
+// diagonal are never loaded; a wave whose rows are all above a tile's keys
+// skips its matrix work.  Workgroups are ordered so that each XCD (which has
+// its own L2) works through whole heads, heaviest query tiles first.
+// Epilogue: O = O / l, LSE = m ln 2 + ln l; a row with no visible key gets
+// O = 0 and LSE = -inf.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -42,29 +49,220 @@ namespace attn {
 namespace {
 
 constexpr float kTau = 8.0f;
+constexpr int kXcds = 8;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 4 bf16 values from LDS through the transposing read: within each group of
+// 16 lanes, lane i receives element (i % 4) of the 8-byte words addressed by
+// lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <int D>
+struct TileCfg {
+    static constexpr int BC = 64;          // keys per tile
+    static constexpr int RB = 2 * D;       // bytes per K/V row in LDS (no padding)
+    static constexpr int CH = D / 8;       // 16-byte chunks per row
+    static constexpr int RP = 256 / RB;    // rows per 256-byte span of the 64 LDS banks
+    static constexpr int TILE = BC * RB;   // bytes of one K or V tile
+    static constexpr int KS = D / 16;      // k-steps of Q K^T
+    static constexpr int DB = D / 32;      // 32-row blocks of O^T
+    // XOR swizzles of the 16-byte chunks of a row (rows stay unpadded so that
+    // the direct global->LDS loads can fill them):
+    //  K: 16 lanes reading one logical chunk of 16 consecutive rows hit 16
+    //     different bank groups;
+    //  V: the transposing reads of 4 rows x 4 chunks hit 16 different groups.
+    static __device__ __forceinline__ int swz_k(int row) { return (row / RP) % CH; }
+    static __device__ __forceinline__ int swz_v(int row) { return 4 * ((row / RP) % (4 / RP)); }
+};
+
+// Score modifier, rolling update, P and O^T += V^T P^T for one 64-key tile.
+// lk / lv: LDS tiles; kaddr[ks]: this lane's byte offset of its K operand
+// chunk for k-step ks (row r); vaddr[db]: byte offset of its transposing-read
+// word for d-block db (rows of key offset 0).
+template <int D, int BIAS, bool MASK>
+__device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk, const char *lv,
+                                             const int (&kaddr)[D / 16], const int (&vaddr)[D / 32],
+                                             const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32],
+                                             float &m_run, float &l_run, int kt0, int qrow, int qpos,
+                                             float slope_l2, int b, int h, int lane) {
+    using C = TileCfg<D>;
+    constexpr bool FOLD = (BIAS == kBiasNone);
+    const int hh = lane >> 5;
+
+    // 1. S^T = K Q^T
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+            s[kb] = mfma32(as_bf16x8(load16(lk + kaddr[ks] + kb * 32 * C::RB)), as_bf16x8(qreg[ks]), s[kb]);
+    }
+
+    // 2. score modifier; tile max (raw scores when the scale is folded)
+    const float sc = p.scale_log2;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = kt0 + kb * 32 + (e >> 3) * 16 + hh * 8 + (e & 7);
+            float x = s[kb][e];
+            if (!FOLD) {
+                x *= sc;
+                if (BIAS == kBiasAlibi) {
+                    x -= slope_l2 * fabsf((float)(qpos - j));
+                } else if (BIAS == kBiasDenseF32 || BIAS == kBiasDenseBf16) {
+                    const int bi = min(qrow, p.Lq - 1);
+                    const int bj = min(j, p.Lk - 1);
+                    const int64_t idx = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
+                                        (int64_t)bi * p.bias_si + (int64_t)bj * p.bias_sj;
+                    float bv;
+                    if (BIAS == kBiasDenseF32)
+                        bv = static_cast<const float *>(p.bias)[idx];
+                    else
+                        bv = bf16_bits_to_f32(static_cast<const uint16_t *>(p.bias)[idx]);
+                    x = fmaf(bv, kLog2e, x);
+                }
+            }
+            if (MASK && (j >= p.Lk || (p.causal && j > qpos))) x = -INFINITY;
+            s[kb][e] = x;
+            mx = fmaxf(mx, x);
+        }
+    }
+    mx = xor32_max(mx);
+    if (FOLD) mx *= sc;   // sc > 0: max commutes with the scaling
+
+    // 3. lazy repair of l and O when the max has grown by more than TAU
+    if (__any(mx > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    // 4. P = 2^(t - m) in fp32, summed in fp32, packed to bf16
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            float p0, p1;
+            if (FOLD) {
+                p0 = exp2_fast(fmaf(s[kb][e], sc, -m_use));
+                p1 = exp2_fast(fmaf(s[kb][e + 1], sc, -m_use));
+            } else {
+                p0 = exp2_fast(s[kb][e] - m_use);
+                p1 = exp2_fast(s[kb][e + 1] - m_use);
+            }
+            l_run += p0 + p1;
+            pk[kb][e >> 1] = pack_bf16x2(p0, p1);
+        }
+    }
+
+    // 5. O^T += V^T P^T: A operand = 8 keys of one d per lane, by two
+    //    transposing reads of 4 keys each (rows +0..3 and +4..7)
+#pragma unroll
+    for (int kk = 0; kk < C::BC / 16; ++kk) {
+        const int kb = kk >> 1;
+        const int half = kk & 1;
+        const bf16x8 bop = as_bf16x8(u32x4{pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2],
+                                           pk[kb][4 * half + 3]});
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(lv + vaddr[db] + kk * 16 * C::RB));
+            const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(lv + vaddr[db] + (kk * 16 + 4) * C::RB));
+            oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bop, oacc[db]);
+        }
+        // keep the scheduler from hoisting every LDS read of the product at once
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// One tile of the rolling update for this wave: skip it when every row of the
+// wave is above the tile's keys, take the masked path only when the tile
+// crosses the causal diagonal or the end of the keys.
+template <int D, int BIAS>
+__device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, const char *lv,
+                                          const int (&kaddr)[D / 16], const int (&vaddr)[D / 32],
+                                          const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float &m_run,
+                                          float &l_run, int kt0, int wrow0, int wrow1, int off, int qrow, int qpos,
+                                          float slope_l2, int b, int h, int lane) {
+    constexpr int BC = TileCfg<D>::BC;
+    const bool active = (wrow0 < p.Lq) && (!p.causal || kt0 <= wrow1 + off);
+    if (!active) return;
+    const bool need_mask = (kt0 + BC > p.Lk) || (p.causal && kt0 + BC - 1 > wrow0 + off);
+    if (need_mask)
+        process_tile<D, BIAS, true>(p, lk, lv, kaddr, vaddr, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b,
+                                    h, lane);
+    else
+        process_tile<D, BIAS, false>(p, lk, lv, kaddr, vaddr, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b,
+                                     h, lane);
+}
+
+// Direct global->LDS loads of K/V tile T_ into the LDS tiles at byte offsets
+// KOFF_ / VOFF_ of the kernel's LDS array: lane
+// fills LDS bytes [i*T*16 + wave*1024 + 16*lane, +16) of each tile from the
+// byte offsets kgoff[i] / vgoff[i] inside the tile.  Rows past the end of K/V
+// fall outside the descriptor's range and read as zero (with overlapping rows
+// they read valid data, which the mask discards).  A macro, because the
+// buffer-to-LDS builtins have to appear in the kernel body itself.
+#define ATTN_ISSUE_TILE_LOADS(T_, KOFF_, VOFF_)                                                                 \
+    do {                                                                                                        \
+        const int j0_ = (T_) * BC;                                                                              \
+        const int nvalid_ = min(BC, p.Lk - j0_);                                                                \
+        const __amdgpu_buffer_rsrc_t rk_ =                                                                      \
+            make_rsrc(kp + (int64_t)j0_ * p.k_sl, (uint32_t)(nvalid_ - 1) * kl_bytes + D * 2);                  \
+        const __amdgpu_buffer_rsrc_t rv_ =                                                                      \
+            make_rsrc(vp + (int64_t)j0_ * p.v_sl, (uint32_t)(nvalid_ - 1) * vl_bytes + D * 2);                  \
+        _Pragma("unroll") for (int i_ = 0; i_ < NC; ++i_) {                                                     \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
+                rk_, (__attribute__((address_space(3))) void *)(lds + (KOFF_) + i_ * T * 16 + wave * 1024), 16,        \
+                (int)kgoff[i_], 0, 0, 0);                                                                            \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
+                rv_, (__attribute__((address_space(3))) void *)(lds + (VOFF_) + i_ * T * 16 + wave * 1024), 16,        \
+                (int)vgoff[i_], 0, 0, 0);                                                                            \
+        }                                                                                                       \
+    } while (0)
+
+// s_waitcnt with vmcnt = 0 and the other counters left alone (gfx9 encoding)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, int NW, int BIAS, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
-    constexpr int BR = 32 * NW;      // query rows per workgroup
-    constexpr int BC = 64;           // keys per tile
-    constexpr int T = NW * 64;       // threads
-    constexpr int KSTR = D + 8;      // LDS row stride of the K tile (elements)
-    constexpr int VSTR = BC + 8;     // LDS row stride of the V^T tile (elements)
-    constexpr int KS = D / 16;       // k-steps of Q K^T
-    constexpr int DB = D / 32;       // 32-row blocks of O^T
-    constexpr int NK = BC * D / 8 / T;   // 16-byte K chunks per thread per tile
-    constexpr int KU = NK;               // keys per V transpose unit
-    static_assert(NK >= 1 && BC * D / 8 == NK * T, "tile does not split evenly");
-    static_assert(KU == 1 || KU == 2 || KU == 4 || KU == 8, "unsupported V unit");
+    using C = TileCfg<D>;
+    constexpr int BR = 32 * NW;          // query rows per workgroup
+    constexpr int BC = C::BC;
+    constexpr int T = NW * 64;           // threads
+    constexpr int NC = C::TILE / (T * 16);   // 16-byte direct loads per thread per tensor per tile
+    static_assert(NC >= 1 && C::TILE == NC * T * 16, "tile does not split evenly");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BC * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * VSTR];
+    // K0, K1, V0, V1 tiles
+    __shared__ __attribute__((aligned(1024))) char lds[4 * C::TILE];
 
+    // work item: XCD-contiguous ranges of a head-major list, heavy tiles first
     const int BH = p.B * p.Hq;
     const int nqt = (p.Lq + BR - 1) / BR;
-    int qt = blockIdx.x / BH;
-    const int bh = blockIdx.x - qt * BH;
-    if (p.causal) qt = nqt - 1 - qt;  // heaviest query tiles first
+    const int nblocks = (int)gridDim.x;
+    int item = blockIdx.x;
+    if (nblocks % kXcds == 0) item = (blockIdx.x % kXcds) * (nblocks / kXcds) + blockIdx.x / kXcds;
+    const int bh = item / nqt;
+    int qt = item - bh * nqt;
+    if (p.causal) qt = nqt - 1 - qt;
     const int b = bh / p.Hq;
     const int h = bh - b * p.Hq;
     const int hk = h / p.G;
@@ -77,6 +275,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     const int hh = lane >> 5;
     const int off = p.Lk - p.Lq;
     const int qrow = q0 + wave * 32 + r;
+    const int qpos = qrow + off;
     const int wrow0 = q0 + wave * 32;
     const int wrow1 = min(wrow0 + 31, p.Lq - 1);
 
@@ -90,179 +289,77 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     const uint16_t *vp = static_cast<const uint16_t *>(p.v) + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
 
     // Q fragment: lane holds row qrow, d = 16*ks + 8*hh .. +7 for each k-step.
-    u32x4 qreg[KS];
+    u32x4 qreg[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = u32x4{0, 0, 0, 0};
     if (qrow < p.Lq) {
         const uint16_t *qr = qp + (int64_t)qrow * p.q_sl + hh * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[ks] = load16(qr + ks * 16);
+        for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = load16(qr + ks * 16);
     }
 
     float slope_l2 = 0.f;
     if (BIAS == kBiasAlibi) slope_l2 = p.slopes[h] * kLog2e;
 
-    // staging registers for the next tile
-    u32x4 kst[NK];
-    u32x4 vst[KU];
-    const int v_kg = tid % (BC / KU);   // V unit: keys KU*v_kg .. +KU-1
-    const int v_dc = tid / (BC / KU);   //         d = 8*v_dc .. +7
+    // per-lane byte offsets, fixed for the whole loop
+    int kaddr[C::KS];   // K operand: row r (+32 per key block), logical chunk 2*ks + hh
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) kaddr[ks] = r * C::RB + (((2 * ks + hh) ^ C::swz_k(r)) * 16);
+    int vaddr[C::DB];   // V transposing read: row 8*vh + sl/4, element 32*db + 16*dh + 4*(sl%4)
+    {
+        const int g = lane >> 4, sl = lane & 15;
+        const int vrow = (g >> 1) * 8 + (sl >> 2);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const int e = db * 32 + (g & 1) * 16 + 4 * (sl & 3);
+            vaddr[db] = vrow * C::RB + (((e >> 3) ^ C::swz_v(vrow)) * 16) + (e & 7) * 2;
+        }
+    }
+    // direct loads: lane fills LDS bytes [i*T*16 + wave*1024 + 16*lane, +16) of each tile
+    uint32_t kgoff[NC], vgoff[NC];
+    const uint32_t kl_bytes = (uint32_t)p.k_sl * 2u;
+    const uint32_t vl_bytes = (uint32_t)p.v_sl * 2u;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int pos = i * T * 16 + wave * 1024 + lane * 16;
+        const int row = pos / C::RB;
+        const int pc = (pos % C::RB) / 16;
+        const int key = (row & ~31) | perm32(row & 31);
+        kgoff[i] = (uint32_t)key * kl_bytes + (uint32_t)((pc ^ C::swz_k(row)) * 16);
+        vgoff[i] = (uint32_t)row * vl_bytes + (uint32_t)((pc ^ C::swz_v(row)) * 16);
+    }
 
-    auto load_tile = [&](int t) {
-        const int kbase = t * BC;
+    f32x16 oacc[C::DB];
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int c = tid + i * T;
-            const int key = c / (D / 8);
-            const int dc = c - key * (D / 8);
-            const int j = kbase + key;
-            kst[i] = (j < p.Lk) ? load16(kp + (int64_t)j * p.k_sl + dc * 8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int j = kbase + v_kg * KU + u;
-            vst[u] = (j < p.Lk) ? load16(vp + (int64_t)j * p.v_sl + v_dc * 8) : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int c = tid + i * T;
-            const int key = c / (D / 8);
-            const int dc = c - key * (D / 8);
-            const int row = (key & ~31) | perm32(key & 31);
-            store16(&lds_k[buf][row * KSTR + dc * 8], kst[i]);
-        }
-        // transpose: V^T[d][keys] for d = 8*v_dc + e
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            const bool odd = e & 1;
-            uint32_t packed[KU / 2 > 0 ? KU / 2 : 1];
-            if (KU == 1) {
-                const uint32_t x = vst[0][w];
-                uint16_t *dst = &lds_v[buf][(v_dc * 8 + e) * VSTR + v_kg];
-                *dst = odd ? (uint16_t)(x >> 16) : (uint16_t)(x & 0xffffu);
-                continue;
-            }
-#pragma unroll
-            for (int u = 0; u < KU / 2; ++u) {
-                const uint32_t x0 = vst[2 * u][w];
-                const uint32_t x1 = vst[2 * u + 1][w];
-                packed[u] = odd ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-            }
-            uint16_t *dst = &lds_v[buf][(v_dc * 8 + e) * VSTR + v_kg * KU];
-            if (KU == 2) {
-                *reinterpret_cast<uint32_t *>(dst) = packed[0];
-            } else if (KU == 4) {
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{packed[0], packed[1]};
-            } else {
-                *reinterpret_cast<u32x4 *>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-            }
-        }
-    };
-
-    f32x16 oacc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
     float m_run = -INFINITY;   // running max, log2 units
     float l_run = 0.f;         // running sum over this lane's half of the keys
 
+    char *const ldk0 = lds, *const ldk1 = lds + C::TILE;
+    char *const ldv0 = lds + 2 * C::TILE, *const ldv1 = lds + 3 * C::TILE;
+
     if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
+        ATTN_ISSUE_TILE_LOADS(0, 0, 2 * C::TILE);
+        wait_vmem();
         __syncthreads();
     }
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
-        const int kt0 = t * BC;
-        const bool active = (wrow0 < p.Lq) && (!p.causal || kt0 <= wrow1 + off);
-        if (active) {
-            const bool need_mask = (kt0 + BC > p.Lk) || (p.causal && kt0 + BC - 1 > wrow0 + off);
-            // 1. S^T = K Q^T
-            f32x16 s[BC / 32];
-#pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-                const uint16_t *kr = &lds_k[buf][(kb * 32 + r) * KSTR + hh * 8];
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    s[kb] = mfma32(as_bf16x8(load16(kr + ks * 16)), as_bf16x8(qreg[ks]), s[kb]);
-            }
-            // 2. score modifier, log2 units; tile max
-            float mx = -INFINITY;
-            const int qpos = qrow + off;
-#pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = kt0 + kb * 32 + (e >> 3) * 16 + hh * 8 + (e & 7);
-                    float x = s[kb][e] * p.scale_log2;
-                    if (BIAS == kBiasAlibi) {
-                        x -= slope_l2 * fabsf((float)(qpos - j));
-                    } else if (BIAS == kBiasDenseF32 || BIAS == kBiasDenseBf16) {
-                        const int bi = min(qrow, p.Lq - 1);
-                        const int bj = min(j, p.Lk - 1);
-                        const int64_t idx = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
-                                            (int64_t)bi * p.bias_si + (int64_t)bj * p.bias_sj;
-                        float bv;
-                        if (BIAS == kBiasDenseF32)
-                            bv = static_cast<const float *>(p.bias)[idx];
-                        else
-                            bv = bf16_bits_to_f32(static_cast<const uint16_t *>(p.bias)[idx]);
-                        x = fmaf(bv, kLog2e, x);
-                    }
-                    if (need_mask && (j >= p.Lk || (p.causal && j > qpos))) x = -INFINITY;
-                    s[kb][e] = x;
-                    mx = fmaxf(mx, x);
-                }
-            }
-            mx = xor32_max(mx);
-            // 3. lazy repair of l and O when the max has grown by more than TAU
-            if (__any(mx > m_run + kTau)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-            // 4. P = 2^(t - m) in fp32, summed in fp32, packed to bf16
-            uint32_t pk[BC / 32][8];
-#pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-                for (int e = 0; e < 16; e += 2) {
-                    const float p0 = exp2_fast(s[kb][e] - m_use);
-                    const float p1 = exp2_fast(s[kb][e + 1] - m_use);
-                    l_run += p0 + p1;
-                    pk[kb][e >> 1] = pack_bf16x2(p0, p1);
-                }
-            }
-            // 5. O^T += V^T P^T
-#pragma unroll
-            for (int kk = 0; kk < BC / 16; ++kk) {
-                const int kb = kk >> 1;
-                const int half = kk & 1;
-                const bf16x8 bop = as_bf16x8(u32x4{pk[kb][4 * half], pk[kb][4 * half + 1],
-                                                   pk[kb][4 * half + 2], pk[kb][4 * half + 3]});
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint16_t *vr = &lds_v[buf][(db * 32 + r) * VSTR + kk * 16 + hh * 8];
-                    oacc[db] = mfma32(as_bf16x8(load16(vr)), bop, oacc[db]);
-                }
-            }
-        }
-        if (t + 1 < ntiles) store_tile(buf ^ 1);
+    // two tiles per trip so that each LDS buffer's address is a constant
+    for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, C::TILE, 3 * C::TILE);
+        tile_step<D, BIAS>(p, ldk0, ldv0, kaddr, vaddr, qreg, oacc, m_run, l_run, t * BC, wrow0, wrow1, off, qrow,
+                           qpos, slope_l2, b, h, lane);
+        wait_vmem();
         __syncthreads();
+        if (t + 1 < ntiles) {
+            if (t + 2 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 2, 0, 2 * C::TILE);
+            tile_step<D, BIAS>(p, ldk1, ldv1, kaddr, vaddr, qreg, oacc, m_run, l_run, (t + 1) * BC, wrow0, wrow1,
+                               off, qrow, qpos, slope_l2, b, h, lane);
+            wait_vmem();
+            __syncthreads();
+        }
     }
 
     // epilogue
@@ -271,7 +368,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     if (qrow < p.Lq) {
         const int64_t obase = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sl;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = db * 32 + i * 8 + hh * 4;
@@ -311,8 +408,11 @@ hipError_t launch_prefill_t(const FwdParams &p, hipStream_t stream) {
 template <int D>
 hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
     constexpr int NW = 4;
-    switch (p.bias_kind) {
+    // the folded-scale path needs a positive scale; otherwise form the score explicitly
+    const int kind = (p.bias_kind == kBiasNone && !(p.scale_log2 > 0.f)) ? kBiasNoneScaled : p.bias_kind;
+    switch (kind) {
         case kBiasNone: return launch_prefill_t<D, NW, kBiasNone>(p, stream);
+        case kBiasNoneScaled: return launch_prefill_t<D, NW, kBiasNoneScaled>(p, stream);
         case kBiasAlibi: return launch_prefill_t<D, NW, kBiasAlibi>(p, stream);
         case kBiasDenseF32: return launch_prefill_t<D, NW, kBiasDenseF32>(p, stream);
         case kBiasDenseBf16: return launch_prefill_t<D, NW, kBiasDenseBf16>(p, stream);
