@@ -147,10 +147,12 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
         l_run *= alpha;
+        // in place, so the accumulators keep their registers across this rarely
+        // taken branch (no copies on the common path)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            for (int e = 0; e < 16; ++e) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(oacc[db][e]) : "v"(alpha));
         m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -193,25 +195,18 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     }
 }
 
-// One tile of the rolling update for this wave: skip it when every row of the
-// wave is above the tile's keys, take the masked path only when the tile
-// crosses the causal diagonal or the end of the keys.
-template <int D, int BIAS>
+// One tile of the rolling update for this wave.  Unmasked tiles lie below the
+// diagonal of every row of the workgroup and inside the keys.  On masked
+// tiles a wave whose rows are all above the tile's keys skips the work.
+template <int D, int BIAS, bool MASK>
 __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, const char *lv,
                                           const int (&kaddr)[D / 16], const int (&vaddr)[D / 32],
                                           const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float &m_run,
                                           float &l_run, int kt0, int wrow0, int wrow1, int off, int qrow, int qpos,
                                           float slope_l2, int b, int h, int lane) {
-    constexpr int BC = TileCfg<D>::BC;
-    const bool active = (wrow0 < p.Lq) && (!p.causal || kt0 <= wrow1 + off);
-    if (!active) return;
-    const bool need_mask = (kt0 + BC > p.Lk) || (p.causal && kt0 + BC - 1 > wrow0 + off);
-    if (need_mask)
-        process_tile<D, BIAS, true>(p, lk, lv, kaddr, vaddr, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b,
-                                    h, lane);
-    else
-        process_tile<D, BIAS, false>(p, lk, lv, kaddr, vaddr, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b,
-                                     h, lane);
+    if (MASK && !((wrow0 < p.Lq) && (!p.causal || kt0 <= wrow1 + off))) return;
+    process_tile<D, BIAS, MASK>(p, lk, lv, kaddr, vaddr, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b, h,
+                                lane);
 }
 
 // Direct global->LDS loads of K/V tile T_ into the LDS tiles at byte offsets
@@ -346,21 +341,45 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
         __syncthreads();
     }
 
-    // two tiles per trip so that each LDS buffer's address is a constant
-    for (int t = 0; t < ntiles; t += 2) {
-        if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, C::TILE, 3 * C::TILE);
-        tile_step<D, BIAS>(p, ldk0, ldv0, kaddr, vaddr, qreg, oacc, m_run, l_run, t * BC, wrow0, wrow1, off, qrow,
-                           qpos, slope_l2, b, h, lane);
+    // Tiles [0, n_full) need no mask for any row of the workgroup: they run
+    // two per trip so that each LDS buffer's address is a constant.  The rest
+    // (the causal diagonal band and the key tail) take the masked path.
+    int n_full = p.Lk / BC;
+    if (p.causal) n_full = min(n_full, max(0, (q0 + off + 1) / BC));
+    n_full = min(n_full, ntiles);
+#define ATTN_STEP(MASK_, BUF_, T_)                                                                               \
+    tile_step<D, BIAS, MASK_>(p, lds + (BUF_) * C::TILE, lds + (2 + (BUF_)) * C::TILE, kaddr, vaddr, qreg, oacc,    \
+                              m_run, l_run, (T_) * BC, wrow0, wrow1, off, qrow, qpos, slope_l2, b, h, lane)
+    int t = 0;
+    for (; t + 1 < n_full; t += 2) {
+        ATTN_ISSUE_TILE_LOADS(t + 1, C::TILE, 3 * C::TILE);
+        ATTN_STEP(false, 0, t);
         wait_vmem();
         __syncthreads();
-        if (t + 1 < ntiles) {
-            if (t + 2 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 2, 0, 2 * C::TILE);
-            tile_step<D, BIAS>(p, ldk1, ldv1, kaddr, vaddr, qreg, oacc, m_run, l_run, (t + 1) * BC, wrow0, wrow1,
-                               off, qrow, qpos, slope_l2, b, h, lane);
-            wait_vmem();
-            __syncthreads();
-        }
+        if (t + 2 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 2, 0, 2 * C::TILE);
+        ATTN_STEP(false, 1, t + 1);
+        wait_vmem();
+        __syncthreads();
     }
+    for (; t < ntiles; ++t) {
+        const bool masked = t >= n_full;
+        if ((t & 1) == 0) {
+            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, C::TILE, 3 * C::TILE);
+            if (masked)
+                ATTN_STEP(true, 0, t);
+            else
+                ATTN_STEP(false, 0, t);
+        } else {
+            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, 0, 2 * C::TILE);
+            if (masked)
+                ATTN_STEP(true, 1, t);
+            else
+                ATTN_STEP(false, 1, t);
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+#undef ATTN_STEP
 
     // epilogue
     const float l_tot = xor32_sum(l_run);
