@@ -209,8 +209,8 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, co
                                 lane);
 }
 
-// Direct global->LDS loads of K/V tile T_ into the LDS tiles at byte offsets
-// KOFF_ / VOFF_ of the kernel's LDS array: lane
+// Direct global->LDS loads of K/V tile T_ into the LDS tile arrays KOFF_ /
+// VOFF_: lane
 // fills LDS bytes [i*T*16 + wave*1024 + 16*lane, +16) of each tile from the
 // byte offsets kgoff[i] / vgoff[i] inside the tile.  Rows past the end of K/V
 // fall outside the descriptor's range and read as zero (with overlapping rows
@@ -226,10 +226,10 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, co
             make_rsrc(vp + (int64_t)j0_ * p.v_sl, (uint32_t)(nvalid_ - 1) * vl_bytes + D * 2);                  \
         _Pragma("unroll") for (int i_ = 0; i_ < NC; ++i_) {                                                     \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
-                rk_, (__attribute__((address_space(3))) void *)(lds + (KOFF_) + i_ * T * 16 + wave * 1024), 16,        \
+                rk_, (__attribute__((address_space(3))) void *)((KOFF_) + i_ * T * 16 + wave * 1024), 16,        \
                 (int)kgoff[i_], 0, 0, 0);                                                                            \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
-                rv_, (__attribute__((address_space(3))) void *)(lds + (VOFF_) + i_ * T * 16 + wave * 1024), 16,        \
+                rv_, (__attribute__((address_space(3))) void *)((VOFF_) + i_ * T * 16 + wave * 1024), 16,        \
                 (int)vgoff[i_], 0, 0, 0);                                                                            \
         }                                                                                                       \
     } while (0)
@@ -246,8 +246,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     constexpr int NC = C::TILE / (T * 16);   // 16-byte direct loads per thread per tensor per tile
     static_assert(NC >= 1 && C::TILE == NC * T * 16, "tile does not split evenly");
 
-    // K0, K1, V0, V1 tiles
-    __shared__ __attribute__((aligned(1024))) char lds[4 * C::TILE];
+    // two K and two V tiles, as separate objects so that the compiler can tell
+    // the tile being filled by the direct loads from the tiles being read
+    // (with one array it waits for the loads before every LDS read)
+    __shared__ __attribute__((aligned(1024))) char lds_k0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_k1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v1[C::TILE];
 
     // work item: XCD-contiguous ranges of a head-major list, heavy tiles first
     const int BH = p.B * p.Hq;
@@ -332,11 +337,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     float m_run = -INFINITY;   // running max, log2 units
     float l_run = 0.f;         // running sum over this lane's half of the keys
 
-    char *const ldk0 = lds, *const ldk1 = lds + C::TILE;
-    char *const ldv0 = lds + 2 * C::TILE, *const ldv1 = lds + 3 * C::TILE;
 
     if (ntiles > 0) {
-        ATTN_ISSUE_TILE_LOADS(0, 0, 2 * C::TILE);
+        ATTN_ISSUE_TILE_LOADS(0, lds_k0, lds_v0);
         wait_vmem();
         __syncthreads();
     }
@@ -348,15 +351,15 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     if (p.causal) n_full = min(n_full, max(0, (q0 + off + 1) / BC));
     n_full = min(n_full, ntiles);
 #define ATTN_STEP(MASK_, BUF_, T_)                                                                               \
-    tile_step<D, BIAS, MASK_>(p, lds + (BUF_) * C::TILE, lds + (2 + (BUF_)) * C::TILE, kaddr, vaddr, qreg, oacc,    \
+    tile_step<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, kaddr, vaddr, qreg, oacc,    \
                               m_run, l_run, (T_) * BC, wrow0, wrow1, off, qrow, qpos, slope_l2, b, h, lane)
     int t = 0;
     for (; t + 1 < n_full; t += 2) {
-        ATTN_ISSUE_TILE_LOADS(t + 1, C::TILE, 3 * C::TILE);
+        ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1);
         ATTN_STEP(false, 0, t);
         wait_vmem();
         __syncthreads();
-        if (t + 2 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 2, 0, 2 * C::TILE);
+        if (t + 2 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 2, lds_k0, lds_v0);
         ATTN_STEP(false, 1, t + 1);
         wait_vmem();
         __syncthreads();
@@ -364,13 +367,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     for (; t < ntiles; ++t) {
         const bool masked = t >= n_full;
         if ((t & 1) == 0) {
-            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, C::TILE, 3 * C::TILE);
+            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1);
             if (masked)
                 ATTN_STEP(true, 0, t);
             else
                 ATTN_STEP(false, 0, t);
         } else {
-            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, 0, 2 * C::TILE);
+            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, lds_k0, lds_v0);
             if (masked)
                 ATTN_STEP(true, 1, t);
             else
