@@ -84,12 +84,12 @@ struct TileCfg {
 };
 
 // Score modifier, rolling update, P and O^T += V^T P^T for one 64-key tile.
-// lk / lv: LDS tiles; kaddr[ks]: this lane's byte offset of its K operand
-// chunk for k-step ks (row r); vaddr[db]: byte offset of its transposing-read
-// word for d-block db (rows of key offset 0).
+// lk / lv: LDS tiles; this lane's K operand chunk for k-step ks is at byte
+// kbase ^ (ks << 5) (+32 rows per key block), its transposing-read word for
+// d-block db at vbase ^ (db << 6) (+ key rows).
 template <int D, int BIAS, bool MASK>
 __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk, const char *lv,
-                                             const int (&kaddr)[D / 16], const int (&vaddr)[D / 32],
+                                             int kbase, int vbase,
                                              const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32],
                                              float &m_run, float &l_run, int kt0, int qrow, int qpos,
                                              float slope_l2, int b, int h, int lane) {
@@ -97,17 +97,25 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     constexpr bool FOLD = (BIAS == kBiasNone);
     const int hh = lane >> 5;
 
-    // 1. S^T = K Q^T
+    // 1. S^T = K Q^T, the two 32-key blocks interleaved (two accumulation
+    //    chains); the K operand reads run 8 matrix-core steps ahead
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-            s[kb] = mfma32(as_bf16x8(load16(lk + kaddr[ks] + kb * 32 * C::RB)), as_bf16x8(qreg[ks]), s[kb]);
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            s[kb] = mfma32(as_bf16x8(load16(lk + ((kbase ^ (ks << 5)) + kb * 32 * C::RB))), as_bf16x8(qreg[ks]), s[kb]);
+    // schedule: operand reads ahead of the matrix core (all of them for D = 64)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 2 * C::KS - 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-
     // 2. score modifier; tile max (raw scores when the scale is folded)
     const float sc = p.scale_log2;
     float mx = -INFINITY;
@@ -186,12 +194,16 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                                            pk[kb][4 * half + 3]});
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(lv + vaddr[db] + kk * 16 * C::RB));
-            const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(lv + vaddr[db] + (kk * 16 + 4) * C::RB));
+            const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(lv + (vbase ^ (db << 6)) + kk * 16 * C::RB));
+            const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(lv + (vbase ^ (db << 6)) + (kk * 16 + 4) * C::RB));
             oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bop, oacc[db]);
         }
-        // keep the scheduler from hoisting every LDS read of the product at once
-        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * 4, 1);
+#pragma unroll
+    for (int i = 0; i < C::BC / 16 * C::DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (i < C::BC / 16 * C::DB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
 }
 
@@ -200,12 +212,12 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
 // tiles a wave whose rows are all above the tile's keys skips the work.
 template <int D, int BIAS, bool MASK>
 __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, const char *lv,
-                                          const int (&kaddr)[D / 16], const int (&vaddr)[D / 32],
+                                          int kbase, int vbase,
                                           const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float &m_run,
                                           float &l_run, int kt0, int wrow0, int wrow1, int off, int qrow, int qpos,
                                           float slope_l2, int b, int h, int lane) {
     if (MASK && !((wrow0 < p.Lq) && (!p.causal || kt0 <= wrow1 + off))) return;
-    process_tile<D, BIAS, MASK>(p, lk, lv, kaddr, vaddr, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b, h,
+    process_tile<D, BIAS, MASK>(p, lk, lv, kbase, vbase, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b, h,
                                 lane);
 }
 
@@ -227,10 +239,10 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, co
         _Pragma("unroll") for (int i_ = 0; i_ < NC; ++i_) {                                                     \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
                 rk_, (__attribute__((address_space(3))) void *)((KOFF_) + i_ * T * 16 + wave * 1024), 16,        \
-                (int)kgoff[i_], 0, 0, 0);                                                                            \
+                (int)kgoff, (int)(i_ * RROWS * kl_bytes), 0, 0);                                                                            \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
                 rv_, (__attribute__((address_space(3))) void *)((VOFF_) + i_ * T * 16 + wave * 1024), 16,        \
-                (int)vgoff[i_], 0, 0, 0);                                                                            \
+                (int)vgoff, (int)(i_ * RROWS * vl_bytes), 0, 0);                                                                            \
         }                                                                                                       \
     } while (0)
 
@@ -301,32 +313,32 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     float slope_l2 = 0.f;
     if (BIAS == kBiasAlibi) slope_l2 = p.slopes[h] * kLog2e;
 
-    // per-lane byte offsets, fixed for the whole loop
-    int kaddr[C::KS];   // K operand: row r (+32 per key block), logical chunk 2*ks + hh
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kaddr[ks] = r * C::RB + (((2 * ks + hh) ^ C::swz_k(r)) * 16);
-    int vaddr[C::DB];   // V transposing read: row 8*vh + sl/4, element 32*db + 16*dh + 4*(sl%4)
+    // per-lane LDS byte offsets: K operand of k-step ks at kbase ^ (ks << 5)
+    // (+32 rows per key block); V transposing read of d-block db at
+    // vbase ^ (db << 6) (+ key rows).  The XOR only touches the swizzled chunk
+    // bits of the row.
+    const int kbase = r * C::RB + ((hh ^ C::swz_k(r)) << 4);
+    int vbase;
     {
         const int g = lane >> 4, sl = lane & 15;
         const int vrow = (g >> 1) * 8 + (sl >> 2);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-            const int e = db * 32 + (g & 1) * 16 + 4 * (sl & 3);
-            vaddr[db] = vrow * C::RB + (((e >> 3) ^ C::swz_v(vrow)) * 16) + (e & 7) * 2;
-        }
+        const int e = (g & 1) * 16 + 4 * (sl & 3);
+        vbase = vrow * C::RB + (((e >> 3) ^ C::swz_v(vrow)) * 16) + (e & 7) * 2;
     }
-    // direct loads: lane fills LDS bytes [i*T*16 + wave*1024 + 16*lane, +16) of each tile
-    uint32_t kgoff[NC], vgoff[NC];
+    // direct loads: round i fills LDS bytes [i*T*16 + wave*1024 + 16*lane, +16)
+    // of a tile; rounds differ by T*16/RB whole rows, so the per-lane source
+    // offset is the same and the round's row offset goes in the scalar offset
+    constexpr int RROWS = T * 16 / C::RB;
     const uint32_t kl_bytes = (uint32_t)p.k_sl * 2u;
     const uint32_t vl_bytes = (uint32_t)p.v_sl * 2u;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int pos = i * T * 16 + wave * 1024 + lane * 16;
+    uint32_t kgoff, vgoff;
+    {
+        const int pos = wave * 1024 + lane * 16;
         const int row = pos / C::RB;
         const int pc = (pos % C::RB) / 16;
         const int key = (row & ~31) | perm32(row & 31);
-        kgoff[i] = (uint32_t)key * kl_bytes + (uint32_t)((pc ^ C::swz_k(row)) * 16);
-        vgoff[i] = (uint32_t)row * vl_bytes + (uint32_t)((pc ^ C::swz_v(row)) * 16);
+        kgoff = (uint32_t)key * kl_bytes + (uint32_t)((pc ^ C::swz_k(row)) * 16);
+        vgoff = (uint32_t)row * vl_bytes + (uint32_t)((pc ^ C::swz_v(row)) * 16);
     }
 
     f32x16 oacc[C::DB];
@@ -351,7 +363,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     if (p.causal) n_full = min(n_full, max(0, (q0 + off + 1) / BC));
     n_full = min(n_full, ntiles);
 #define ATTN_STEP(MASK_, BUF_, T_)                                                                               \
-    tile_step<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, kaddr, vaddr, qreg, oacc,    \
+    tile_step<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, kbase, vbase, qreg, oacc,    \
                               m_run, l_run, (T_) * BC, wrow0, wrow1, off, qrow, qpos, slope_l2, b, h, lane)
     int t = 0;
     for (; t + 1 < n_full; t += 2) {
