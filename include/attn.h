@@ -146,9 +146,11 @@ attn_status attn_splitk_combine(const float *o_part, const float *m_part, const 
 
 /*
  * attn_decode_choose_splits -- split count for attn_fwd_decode_splitk (pure
- * host function, no HIP call).  Picks the number of key chunks so that the
- * B * Hkv * ceil(Lq*Hq/Hkv / 32) * num_splits workgroups fill cu_count compute
- * units several times over while keeping at least 256 keys per chunk (an
+ * host function, no HIP call).  Picks the smallest number of key chunks for
+ * which the B * Hkv * ceil(Lq*Hq/Hkv / 32) * num_splits workgroups give every
+ * one of cu_count compute units a workgroup (each workgroup streams its chunk
+ * with enough loads in flight to keep its share of HBM busy), while keeping
+ * at least 256 keys per chunk (an
  * under-filled grid is what the Mirage lecture notes, section 7.1, measure as
  * the cost of fixed grid heuristics).  Returns >= 1; 1 when Lk <= 256.
  */

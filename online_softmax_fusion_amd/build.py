@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn_mi355x.so")
 SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip", "combine.hip", "attn_api.cpp"]
+# per-source device flags: the decode kernel keeps its matrix-core results in
+# ordinary VGPRs (its LDS use leaves one workgroup per CU, and the compiler's
+# default then moves the accumulators to AGPRs and back on every loop trip)
+EXTRA = {"decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -34,6 +38,7 @@ def _compile(src: str, verbose: bool) -> str:
            os.path.join(CSRC, src), "-o", obj, "-I", os.path.join(ROOT, "include")]
     if src.endswith(".hip"):
         cmd += ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    cmd += EXTRA.get(src, [])
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -188,7 +188,8 @@ int32_t attn_decode_choose_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq
     const int64_t cu = cu_count > 0 ? cu_count : 256;
     const int64_t rblocks = ((Hq / Hkv) * Lq + 31) / 32;
     const int64_t units = B * Hkv * rblocks;
-    const int64_t target = 2 * cu;               // two resident workgroups per compute unit
+    const int64_t target = cu;                   // one workgroup per compute unit (the decode
+                                                 // kernel's LDS stages hold one per CU at D = 128)
     int64_t S = (target + units - 1) / units;
     const int64_t max_by_len = Lk / 256;         // at least 256 keys per chunk
     if (S > max_by_len) S = max_by_len;

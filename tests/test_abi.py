@@ -137,9 +137,9 @@ def test_empty_problem_is_ok_without_launch(lib):
 
 
 def test_choose_splits(lib):
-    # fills two workgroups per compute unit, at least 256 keys per chunk
-    assert lib.attn_decode_choose_splits(1, 8, 8, 1, 32768, 256) == 64
-    assert lib.attn_decode_choose_splits(16, 32, 8, 1, 32768, 256) == 4
+    # fills one workgroup per compute unit, at least 256 keys per chunk
+    assert lib.attn_decode_choose_splits(1, 8, 8, 1, 32768, 256) == 32
+    assert lib.attn_decode_choose_splits(16, 32, 8, 1, 32768, 256) == 2
     assert lib.attn_decode_choose_splits(1, 8, 8, 1, 200, 256) == 1
     assert lib.attn_decode_choose_splits(1, 8, 8, 1, 1024, 256) == 4
     assert lib.attn_decode_choose_splits(1, 8, 3, 1, 4096, 256) == 1   # invalid grouping -> 1

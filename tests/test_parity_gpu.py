@@ -265,3 +265,60 @@ def test_decode_choose_splits_on_device():
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale())
     compare(o, lse, O_ref, L_ref, "bf16", "auto splits")
     assert S >= 1
+
+
+@pytest.mark.parametrize("rows_shape,D,S", [((8, 64, 5), 128, 3), ((3, 40, 20), 64, 33), ((1, 2, 1), 128, 70)])
+def test_combine_parity_synthetic_partials(rows_shape, D, S):
+    """The combine alone on synthetic partials (both launch shapes: few rows
+    and > 2048 rows), with empty chunks (m = -inf) and whole rows without keys,
+    against the fp64 combine of the oracle."""
+    B, Hq, Lq = rows_shape
+    print("combine case", rows_shape, D, S, flush=True)
+    g = torch.Generator().manual_seed(B * 1000 + Hq * 10 + S)
+    op = torch.randn((B, Hq, Lq, S, D), generator=g)
+    mp = 3.0 * torch.randn((B, Hq, Lq, S), generator=g)
+    lp = torch.rand((B, Hq, Lq, S), generator=g) * 50 + 0.5
+    empty = torch.rand((B, Hq, Lq, S), generator=g) < 0.2
+    mp[empty] = -math.inf
+    lp[empty] = 0.0
+    op[empty] = 0.0
+    mp[0, 0, 0, :] = -math.inf           # a row that saw no key at all
+    lp[0, 0, 0, :] = 0.0
+    op[0, 0, 0, :, :] = 0.0
+    o, lse = attn.attn_splitk_combine(op.cuda(), mp.cuda(), lp.cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Oc, Lc = oracle.splitk_combine(op, mp, lp)
+    compare(o, lse, Oc, Lc, "f32", "combine %s" % (rows_shape,))
+    assert torch.all(o[0, 0, 0] == 0) and lse[0, 0, 0].item() == -math.inf
+
+
+def test_decode_graph_replay():
+    """The decode step (local step + combine) captured in a HIP graph gives the
+    eager result on every replay, with other eager work between replays."""
+    w, q, k, v, _, _ = inputs(2, 8, 2, 1, 3000, 128, "bf16", seed=9)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    S = 6
+    op = torch.empty((2, 8, 1, S, 128), dtype=torch.float32, device="cuda")
+    mp = torch.empty((2, 8, 1, S), dtype=torch.float32, device="cuda")
+    lp = torch.empty_like(mp)
+    o = torch.empty_like(qg)
+    lse = torch.empty((2, 8, 1), dtype=torch.float32, device="cuda")
+
+    def step():
+        attn.attn_fwd_decode_splitk(qg, kg, vg, S, w.softmax_scale(), o_part=op, m_part=mp, l_part=lp)
+        attn.attn_splitk_combine(op, mp, lp, out=o, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = o.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        o.zero_()
+        lse.zero_()
+        attn.decode(qg * 0.5, kg, vg, 3, w.softmax_scale())   # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), "replay %d" % r
