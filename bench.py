@@ -112,7 +112,24 @@ def measured_traffic(kernel: str, workload: str, sources) -> "int | None":
 # ----------------------------------------------------------------------------
 # legs
 # ----------------------------------------------------------------------------
-def time_prefill(w, steps, warmup):
+def warm_up(fn, warmup, seconds):
+    """W untimed steps, continued until `seconds` of GPU work have run, so the
+    timed steps start at settled clocks (the first second or so of work on an
+    idle GPU runs measurably slower)."""
+    import torch
+
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+def time_prefill(w, steps, warmup, warm_s=1.0):
     import torch
     import synth
     import online_softmax_fusion_amd as attn
@@ -125,9 +142,8 @@ def time_prefill(w, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
     scale = w.softmax_scale()
-    for _ in range(warmup):
-        attn.attn_fwd_prefill(q, k, v, scale, w.causal, out=o, lse=lse, **kw)
-    torch.cuda.synchronize()
+    n = warm_up(lambda i: attn.attn_fwd_prefill(q, k, v, scale, w.causal, out=o, lse=lse, **kw), warmup, warm_s)
+    log("prefill: %d untimed warm-up steps" % n)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -148,7 +164,7 @@ def time_prefill(w, steps, warmup):
     return wall / steps, avg_ms * 1e-3, flops, durs
 
 
-def time_decode(w, steps, warmup):
+def time_decode(w, steps, warmup, warm_s=1.0):
     """Decode step = split-K local step + combine, issued eagerly; the kernel
     time comes from HIP events around the local step."""
     import torch
@@ -179,9 +195,8 @@ def time_decode(w, steps, warmup):
             evs[1].record(torch.cuda.current_stream())
         attn.attn_splitk_combine(op, mp, lp, out=o, lse=lse)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    n = warm_up(step, warmup, warm_s)
+    log("decode: %d untimed warm-up steps" % n)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
@@ -229,11 +244,69 @@ def cpu_baseline(w, budget_s=15.0):
                       (n, G, w.Lq, w.Lk, ", causal" if w.causal else "", w.D, w.name, t1)}
 
 
+def _counter_kib(csv_path, counter, kernel_substr):
+    """Mean value of `counter` (KiB) over the dispatches whose kernel name
+    contains `kernel_substr` in a rocprofv3 counter_collection.csv."""
+    import csv
+
+    vals = []
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise ValueError("no %s samples for %s in %s" % (counter, kernel_substr, csv_path))
+    return sum(vals) / len(vals)
+
+
+def traffic_table(d):
+    """HBM bytes per launch of the two kernels timed by a default bench run,
+    from FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same
+    counters read for a plain device copy of known size."""
+    import glob
+    import synth
+
+    def csv_of(sub):
+        hits = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not hits:
+            raise FileNotFoundError("no counter_collection.csv under %s" % os.path.join(d, sub))
+        return hits[0]
+
+    copy_bytes = 1 << 30
+    cf = _counter_kib(csv_of("cfetch"), "FETCH_SIZE", "copyBuffer")
+    cw = _counter_kib(csv_of("cwrite"), "WRITE_SIZE", "copyBuffer")
+    fscale, wscale = copy_bytes / 1024.0 / cf, copy_bytes / 1024.0 / cw
+    out = {"_about": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per "
+                     "dispatch, mean over the dispatches of the run), each scaled by the factor that makes the "
+                     "same counter read the known size of a plain 1 GiB device copy (bench.py "
+                     "--copy-calibration). source_digest ties an entry to the kernel source it was measured on; "
+                     "bench.py reports null traffic once that source changes.",
+           "calibration": {"copy_bytes": copy_bytes, "fetch_kib_per_copy": cf, "write_kib_per_copy": cw,
+                           "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5)}}
+    wp, wd = synth.C2_CAUSAL, synth.C4_DECODE
+    S = wd.splits
+    entries = [("prefill_bf16_kernel", wp, PREFILL_SOURCES,
+                prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.Lq, wp.Lk, wp.D)),
+               ("decode_bf16_kernel", wd, DECODE_SOURCES,
+                decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S))]
+    for kernel, w, srcs, alg in entries:
+        fk = _counter_kib(csv_of("fetch"), "FETCH_SIZE", kernel)
+        wk = _counter_kib(csv_of("write"), "WRITE_SIZE", kernel)
+        fb, wb = int(round(fk * 1024 * fscale)), int(round(wk * 1024 * wscale))
+        out[kernel] = {"workload": w.name, "source_digest": source_digest(srcs),
+                       "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                       "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
+                       "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="keep warming up (untimed) until this much time has passed")
     ap.add_argument("--prefill", default=None, help="prefill workload name (default: causal B4 H32 L4096)")
     ap.add_argument("--decode", default=None, help="decode workload name (default: GQA B16 Lk32768)")
     ap.add_argument("--splits", type=int, default=None, help="override the decode split count")
@@ -241,7 +314,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--traffic-table", metavar="DIR", default=None,
+                    help="only summarise the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR (fetch/, write/, "
+                         "cfetch/, cwrite/) into the per-kernel traffic table, printed as JSON")
     args = ap.parse_args()
+    if args.traffic_table:
+        print(json.dumps(traffic_table(args.traffic_table), indent=1))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -273,8 +352,8 @@ def main():
         wd = wd.with_(splits=args.splits)
 
     torch.cuda.synchronize()
-    step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup)
-    d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup)
+    step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup, args.warm_seconds)
+    d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup, args.warm_seconds)
 
     p_tflops = flops / step_s / 1e12
     p_kern_tflops = flops / kern_s / 1e12
