@@ -281,7 +281,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     const int q0 = qt * BR;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches on it stay scalar
     const int lane = tid & 63;
     const int r = lane & 31;
     const int hh = lane >> 5;

@@ -45,6 +45,7 @@ def load_path(path: str):
     lib = ctypes.CDLL(path)
     i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
     lib.oracle_attention.argtypes = [i64, i64, i64, i64, i64, i64, vp, vp, vp, dbl, ctypes.c_int,
+                                     dbl, ctypes.c_int, i64, i64,
                                      ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, ctypes.c_int]
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_splitk_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
@@ -75,13 +76,16 @@ def default_threads() -> int:
 
 
 def attention(q, k, v, scale: float, causal: bool = False, *, bias=None,
-              alibi_slopes=None, rows: Optional[Sequence[int]] = None,
-              threads: Optional[int] = None, lib=None):
+              alibi_slopes=None, softcap: float = 0.0, window: Optional[Sequence[int]] = None,
+              rows: Optional[Sequence[int]] = None, threads: Optional[int] = None, lib=None):
     """fp64 O [rows, D] and LSE [rows] of attention over q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D].
 
     ``bias`` is an additive score bias broadcastable to [B, Hq, Lq, Lk] (numpy or
     torch; size-1 dims broadcast).  ``alibi_slopes`` [Hq] selects the ALiBi bias
-    -slope[h] * |i + Lk - Lq - j| instead.  ``rows`` selects flat row ids
+    -slope[h] * |i + Lk - Lq - j| instead.  ``softcap`` > 0 bounds the scaled
+    score to softcap * tanh(score / softcap) before the bias.  ``window`` =
+    (left, right) keeps only keys j with p - left <= j <= p + right, p = i + Lk
+    - Lq (a negative bound is unbounded).  ``rows`` selects flat row ids
     (b*Hq + h)*Lq + i; by default every row is returned, in order, and O is
     reshaped to [B, Hq, Lq, D] and LSE to [B, Hq, Lq].
     """
@@ -123,7 +127,11 @@ def attention(q, k, v, scale: float, causal: bool = False, *, bias=None,
     o = np.zeros((max(n, 0), D), dtype=np.float64)
     lse = np.zeros((max(n, 0),), dtype=np.float64)
     rc = lib.oracle_attention(B, Hq, Hkv, Lq, Lk, D, _ptr(qa), _ptr(ka), _ptr(va),
-                              float(scale), int(bool(causal)), kind, _ptr(ba), _ptr(strides),
+                              float(scale), int(bool(causal)), float(softcap),
+                              0 if window is None else 1,
+                              -1 if window is None else int(window[0]),
+                              -1 if window is None else int(window[1]),
+                              kind, _ptr(ba), _ptr(strides),
                               _ptr(sa), _ptr(ra), n, _ptr(o), _ptr(lse),
                               int(threads or default_threads()))
     if rc != 0:

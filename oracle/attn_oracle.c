@@ -33,8 +33,18 @@
  *                  query heads share one K, V pair)
  *   position       p  = i + (Lk - Lq)       (queries aligned to the end of the
  *                  keys: a decode query sees the whole cache)
- *   visible keys   all j, or j <= p when causal
- *   score          s_j = scale * sum_d q[d] k_j[d] + bias(b, h, i, j)
+ *   visible keys   all j in [0, Lk); j <= p when causal; with a window,
+ *                  also p - window_left <= j <= p + window_right (a negative
+ *                  bound is unbounded).  The pages only name the sliding
+ *                  Window operator ([Neptune notes] section 9); the bounds
+ *                  follow the usual local-attention reading, relative to the
+ *                  query's position p.
+ *   score          t_j = scale * sum_d q[d] k_j[d]
+ *                  soft cap (when softcap > 0): t_j = softcap * tanh(t_j / softcap)
+ *                  (the SoftCap operator of [Neptune notes] section 9; the page
+ *                  names it only, this is the plain reading: a smooth bound of
+ *                  the scaled score to (-softcap, softcap), before any bias)
+ *                  s_j = t_j + bias(b, h, i, j)
  *                  bias: none; dense tensor (element strides, 0 = broadcast);
  *                  or ALiBi  -slope[h] * |p - j|
  *   pass 1         m = max_j s_j
@@ -61,6 +71,9 @@ typedef struct {
     const float *q, *k, *v;
     double scale;
     int causal;
+    double softcap;            /* > 0: cap the scaled score */
+    int window;                /* 1: apply window_left / window_right */
+    int64_t window_left, window_right;
     int bias_kind;
     const float *bias;
     int64_t bias_strides[4];
@@ -87,25 +100,27 @@ static void oracle_row(const oracle_job *J, int64_t flat, double *o, double *lse
     const float *kbase = J->k + (b * J->Hkv + hk) * J->Lk * D;
     const float *vbase = J->v + (b * J->Hkv + hk) * J->Lk * D;
 
-    int64_t nvis = J->Lk;
-    if (J->causal) {
-        nvis = p + 1;
-        if (nvis < 0) nvis = 0;
-        if (nvis > J->Lk) nvis = J->Lk;
+    /* the visible keys form one interval [jlo, jhi) */
+    int64_t jlo = 0, jhi = J->Lk;
+    if (J->causal && p + 1 < jhi) jhi = p + 1;
+    if (J->window) {
+        if (J->window_left >= 0 && p - J->window_left > jlo) jlo = p - J->window_left;
+        if (J->window_right >= 0 && p + J->window_right + 1 < jhi) jhi = p + J->window_right + 1;
     }
 
     for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-    if (nvis == 0) {
+    if (jhi <= jlo) {
         *lse = -INFINITY;
         return;
     }
 
-    /* scores of the visible keys */
-    for (int64_t j = 0; j < nvis; ++j) {
+    /* scores of the visible keys (s[j - jlo]) */
+    for (int64_t j = jlo; j < jhi; ++j) {
         const float *krow = kbase + j * D;
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (double)krow[d];
         double sj = J->scale * dot;
+        if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);
         if (J->bias_kind == ORACLE_BIAS_DENSE) {
             const int64_t *st = J->bias_strides;
             sj += (double)J->bias[b * st[0] + h * st[1] + i * st[2] + j * st[3]];
@@ -114,13 +129,13 @@ static void oracle_row(const oracle_job *J, int64_t flat, double *o, double *lse
             if (dist < 0) dist = -dist;
             sj += -(double)J->slopes[h] * dist;
         }
-        s[j] = sj;
+        s[j - jlo] = sj;
     }
 
     /* pass 1: the row maximum */
     double m = -INFINITY;
-    for (int64_t j = 0; j < nvis; ++j)
-        if (s[j] > m) m = s[j];
+    for (int64_t j = jlo; j < jhi; ++j)
+        if (s[j - jlo] > m) m = s[j - jlo];
     if (m == -INFINITY) {          /* every visible score is -inf (a -inf bias) */
         *lse = -INFINITY;
         return;
@@ -128,8 +143,8 @@ static void oracle_row(const oracle_job *J, int64_t flat, double *o, double *lse
 
     /* pass 2: exponentials, their sum, and the weighted sum of values */
     double l = 0.0;
-    for (int64_t j = 0; j < nvis; ++j) {
-        const double e = exp(s[j] - m);
+    for (int64_t j = jlo; j < jhi; ++j) {
+        const double e = exp(s[j - jlo] - m);
         l += e;
         const float *vrow = vbase + j * D;
         for (int64_t d = 0; d < D; ++d) o[d] += e * (double)vrow[d];
@@ -162,6 +177,8 @@ static void *oracle_worker(void *arg)
  * oracle_attention: O and LSE for the requested rows.
  *   q [B,Hq,Lq,D], k and v [B,Hkv,Lk,D]: contiguous fp32.
  *   scale: the softmax scale (pass the fp32 value the device receives).
+ *   softcap: > 0 caps the scaled score (0 = off).
+ *   window: 1 applies window_left / window_right (negative = unbounded), 0 = no window.
  *   bias_kind 0 none / 1 dense (bias + strides in elements, b,h,i,j) / 2 ALiBi (slopes[Hq]).
  *   rows: flat row ids (b*Hq + h)*Lq + i, or NULL for all B*Hq*Lq rows in order.
  *   o [nrows][D] and lse [nrows] are written in fp64.
@@ -169,7 +186,8 @@ static void *oracle_worker(void *arg)
  */
 int oracle_attention(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                      const float *q, const float *k, const float *v,
-                     double scale, int causal,
+                     double scale, int causal, double softcap,
+                     int window, int64_t window_left, int64_t window_right,
                      int bias_kind, const float *bias, const int64_t *bias_strides,
                      const float *slopes,
                      const int64_t *rows, int64_t nrows,
@@ -182,6 +200,7 @@ int oracle_attention(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
     if (bias_kind == ORACLE_BIAS_DENSE && (!bias || !bias_strides)) return -1;
     if (bias_kind == ORACLE_BIAS_ALIBI && !slopes) return -1;
     if (bias_kind < 0 || bias_kind > 2) return -1;
+    if (!(softcap >= 0.0) || window < 0 || window > 1) return -1;
 
     const int64_t total = B * Hq * Lq;
     if (!rows) nrows = total;
@@ -192,6 +211,8 @@ int oracle_attention(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
     J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Lq = Lq; J.Lk = Lk; J.D = D;
     J.q = q; J.k = k; J.v = v;
     J.scale = scale; J.causal = causal;
+    J.softcap = softcap; J.window = window;
+    J.window_left = window_left; J.window_right = window_right;
     J.bias_kind = bias_kind; J.bias = bias; J.slopes = slopes;
     for (int t = 0; t < 4; ++t) J.bias_strides[t] = bias_strides ? bias_strides[t] : 0;
     J.rows = rows; J.nrows = nrows;

@@ -42,7 +42,7 @@ RNG = np.random.default_rng(20261202)
 # ----------------------------------------------------------------------------
 # independent brute force: full score matrix through scipy
 # ----------------------------------------------------------------------------
-def brute(q, k, v, scale, causal=False, bias=None, slopes=None):
+def brute(q, k, v, scale, causal=False, bias=None, slopes=None, softcap=0.0, window=None):
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, Hq, Lq, D = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
@@ -50,6 +50,8 @@ def brute(q, k, v, scale, causal=False, bias=None, slopes=None):
     kk = np.repeat(k, G, axis=1)
     vv = np.repeat(v, G, axis=1)
     S = scale * np.matmul(q, np.swapaxes(kk, -1, -2))
+    if softcap > 0:
+        S = softcap * np.tanh(S / softcap)
     pos = np.arange(Lq)[:, None] + (Lk - Lq)
     keys = np.arange(Lk)[None, :]
     if bias is not None:
@@ -58,6 +60,12 @@ def brute(q, k, v, scale, causal=False, bias=None, slopes=None):
         S = S - np.asarray(slopes, dtype=np.float64)[None, :, None, None] * np.abs(pos - keys)
     if causal:
         S = np.where(keys > pos, -np.inf, S)
+    if window is not None:
+        wl, wr = window
+        if wl >= 0:
+            S = np.where(keys < pos - wl, -np.inf, S)
+        if wr >= 0:
+            S = np.where(keys > pos + wr, -np.inf, S)
     lse = logsumexp(S, axis=-1)
     empty = np.isneginf(lse)
     S_safe = np.where(empty[..., None], 0.0, S)
@@ -344,6 +352,120 @@ BRUTE_CASES = [
 ]
 
 
+# SoftCap and Window (Neptune notes section 9 names both operators; readings:
+# cap = c * tanh(score / c) on the scaled score before any bias; window keeps
+# keys p - left <= j <= p + right, negative = unbounded)
+MOD_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, scale, causal, bias, softcap, window
+    (1, 2, 1, 20, 20, 8, 1.5, False, None, 3.0, None),
+    (2, 2, 2, 17, 30, 8, 2.0, True, "dense", 2.5, None),
+    (1, 4, 2, 24, 24, 8, 0.5, True, None, 0.0, (5, -1)),
+    (1, 2, 2, 19, 33, 4, 0.7, False, None, 0.0, (3, 6)),
+    (2, 4, 4, 16, 40, 8, 0.4, True, "alibi", 4.0, (7, 0)),
+    (1, 2, 1, 12, 12, 8, 0.9, False, None, 1.0, (0, 0)),
+    (1, 1, 1, 10, 25, 4, 1.0, True, None, 0.0, (2, -1)),     # rows whose window is inside the causal range
+    (1, 1, 1, 8, 8, 4, 1.0, False, None, 0.0, (-1, 2)),      # right bound only
+]
+
+
+def _mod_inputs(case, rng):
+    B, Hq, Hkv, Lq, Lk, D, scale, causal, bias_kind, softcap, window = case
+    q = (rng.standard_normal((B, Hq, Lq, D)) * 2).astype(np.float32)
+    k = (rng.standard_normal((B, Hkv, Lk, D)) * 2).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, Lk, D)).astype(np.float32)
+    kw, bkw = {"softcap": softcap, "window": window}, {"softcap": softcap, "window": window}
+    if bias_kind == "dense":
+        bias = rng.standard_normal((B, Hq, Lq, Lk)).astype(np.float32)
+        kw["bias"] = bkw["bias"] = bias
+    elif bias_kind == "alibi":
+        slopes = np.power(2.0, -8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        kw["alibi_slopes"] = bkw["slopes"] = slopes
+    return q, k, v, scale, causal, kw, bkw
+
+
+@pytest.mark.parametrize("case", MOD_CASES, ids=[str(i) for i in range(len(MOD_CASES))])
+def test_brute_force_softcap_window(case):
+    q, k, v, scale, causal, kw, bkw = _mod_inputs(case, np.random.default_rng(23))
+    O, lse = oracle.attention(q, k, v, scale, causal, **kw)
+    Ob, lb = brute(q, k, v, scale, causal, **bkw)
+    assert_close(O, Ob, 1e-12, "O")
+    assert_close(lse, lb, 1e-12, "LSE")
+
+
+def test_softcap_closed_form_two_keys():
+    """tanh(ln(3) / 2) = (3 - 1) / (3 + 1) = 1/2, so with cap c = 2 a scaled
+    score of ln 3 is capped to exactly 1: against a score of 0 the weights are
+    e / (e + 1) and 1 / (e + 1), and LSE = ln(e + 1).  (ln 3 is stored in fp32,
+    which moves the capped score by ~1e-7.)"""
+    q = np.array([[[[1.0, 0.0]]]], np.float32)
+    k = np.array([[[[np.log(3.0), 0.0], [0.0, 0.0]]]], np.float32)
+    v = np.array([[[[1.0, 0.0], [0.0, 1.0]]]], np.float32)
+    O, lse = oracle.attention(q, k, v, 1.0, softcap=2.0)
+    e = np.e
+    assert_close(O.reshape(2), np.array([e / (e + 1), 1 / (e + 1)]), 1e-7, "O")
+    assert_close(lse.reshape(1), np.array([np.log(e + 1)]), 1e-7, "LSE")
+    # a huge score saturates at the cap: weights e^c / (e^c + 1) for c = 1
+    k2 = np.array([[[[1000.0, 0.0], [0.0, 0.0]]]], np.float32)
+    O2, _ = oracle.attention(q, k2, v, 1.0, softcap=1.0)
+    assert_close(O2.reshape(2), np.array([e / (e + 1), 1 / (e + 1)]), 1e-15, "saturated O")
+
+
+def test_softcap_limit_and_bound():
+    """A cap far above every score changes nothing (to fp64 rounding); with a
+    cap c every weight ratio inside a row is at most e^(2c)."""
+    rng = np.random.default_rng(3)
+    q, k, v = rnd(1, 2, 12, 8, scale=2), rnd(1, 2, 12, 8, scale=2), rnd(1, 2, 12, 8)
+    O0, l0 = oracle.attention(q, k, v, 0.5)
+    O1, l1 = oracle.attention(q, k, v, 0.5, softcap=1e7)
+    assert_close(O1, O0, 1e-9, "O")
+    assert_close(l1, l0, 1e-9, "LSE")
+    # weights through V = identity (D = Lk)
+    L = 16
+    q = (rng.standard_normal((1, 1, L, L)) * 50).astype(np.float32)
+    k = (rng.standard_normal((1, 1, L, L)) * 50).astype(np.float32)
+    eye = np.eye(L, dtype=np.float32)[None, None]
+    W, _ = oracle.attention(q, k, eye, 1.0, softcap=1.5)
+    assert np.allclose(W.sum(-1), 1.0, atol=1e-12)
+    ratio = W.max(-1) / W.min(-1)
+    assert np.all(ratio <= np.exp(2 * 1.5) * (1 + 1e-12))
+
+
+def test_window_zero_is_the_diagonal():
+    """Window (0, 0) leaves one key per row, j = p: O is that key's V row and
+    LSE its own score."""
+    q, k, v = rnd(1, 2, 9, 4), rnd(1, 2, 13, 4), rnd(1, 2, 13, 4)
+    O, lse = oracle.attention(q, k, v, 0.5, window=(0, 0))
+    p = np.arange(9) + 4
+    assert np.array_equal(O, v[:, :, p, :].astype(np.float64))
+    s = 0.5 * np.einsum("bhid,bhid->bhi", q.astype(np.float64), k[:, :, p, :].astype(np.float64))
+    assert_close(lse, s, 1e-12, "LSE")
+
+
+def test_window_equals_attention_on_the_key_slice():
+    """A windowed row equals unmasked attention of that query over exactly the
+    keys its window keeps (the oracle's own unwindowed path, pinned above)."""
+    q, k, v = rnd(1, 1, 11, 8), rnd(1, 1, 30, 8), rnd(1, 1, 30, 8)
+    for wl, wr in ((4, 2), (0, 5), (6, -1), (-1, 3)):
+        O, lse = oracle.attention(q, k, v, 0.4, window=(wl, wr))
+        for i in range(11):
+            p = i + 19
+            lo = 0 if wl < 0 else max(0, p - wl)
+            hi = 30 if wr < 0 else min(30, p + wr + 1)
+            Os, ls = oracle.attention(q[:, :, i:i + 1], k[:, :, lo:hi], v[:, :, lo:hi], 0.4)
+            assert_close(O[0, 0, i], Os[0, 0, 0], 1e-14, "O row %d" % i)
+            assert_close(lse[0, 0, i], ls[0, 0, 0], 1e-14, "LSE row %d" % i)
+
+
+def test_window_unbounded_is_plain_and_causal():
+    q, k, v = rnd(2, 2, 10, 8), rnd(2, 2, 14, 8), rnd(2, 2, 14, 8)
+    O0, l0 = oracle.attention(q, k, v, 0.3)
+    O1, l1 = oracle.attention(q, k, v, 0.3, window=(100, 100))
+    assert np.array_equal(O0, O1) and np.array_equal(l0, l1)
+    Oc, lc = oracle.attention(q, k, v, 0.3, causal=True)
+    Ow, lw = oracle.attention(q, k, v, 0.3, window=(-1, 0))
+    assert np.array_equal(Oc, Ow) and np.array_equal(lc, lw)
+
+
 @pytest.mark.parametrize("case", BRUTE_CASES, ids=[str(i) for i in range(len(BRUTE_CASES))])
 def test_brute_force(case):
     B, Hq, Hkv, Lq, Lk, D, scale, causal, bias_kind = case
@@ -504,7 +626,15 @@ MUTANTS = {
     "kv_head_modulo": ("const int64_t hk = h / G;", "const int64_t hk = h % J->Hkv;"),
     "dropped_scale": ("double sj = J->scale * dot;", "double sj = dot;"),
     "alibi_sign": ("sj += -(double)J->slopes[h] * dist;", "sj += (double)J->slopes[h] * dist;"),
-    "causal_off_by_one": ("nvis = p + 1;", "nvis = p;"),
+    "causal_off_by_one": ("if (J->causal && p + 1 < jhi) jhi = p + 1;", "if (J->causal && p < jhi) jhi = p;"),
+    "softcap_undivided": ("sj = J->softcap * tanh(sj / J->softcap);", "sj = J->softcap * tanh(sj);"),
+    "softcap_ignored": ("        if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);\n", "\n"),
+    "softcap_after_bias": ("        if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);\n"
+                           "        if (J->bias_kind == ORACLE_BIAS_DENSE) {",
+                           "        if (J->bias_kind == ORACLE_BIAS_DENSE) {"
+                           " if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);"),
+    "window_left_off_by_one": ("jlo = p - J->window_left;", "jlo = p - J->window_left + 1;"),
+    "window_right_off_by_one": ("jhi = p + J->window_right + 1;", "jhi = p + J->window_right;"),
     "causal_top_left": ("const int64_t p = i + (J->Lk - J->Lq);", "const int64_t p = i;"),
     "lse_log2": ("*lse = m + log(l);", "*lse = m + log2(l);"),
     "missing_normalise": ("for (int64_t d = 0; d < D; ++d) o[d] /= l;", ";"),
@@ -531,6 +661,12 @@ def _pin_suite(lib):
             elif bias_kind == "alibi":
                 slopes = np.power(2.0, -8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
                 kw["alibi_slopes"] = bkw["slopes"] = slopes
+            O, lse = oracle.attention(q, k, v, scale, causal, lib=lib, **kw)
+            Ob, lb = brute(q, k, v, scale, causal, **bkw)
+            assert_close(O, Ob, 1e-12, "O")
+            assert_close(lse, lb, 1e-12, "LSE")
+        for case in MOD_CASES:
+            q, k, v, scale, causal, kw, bkw = _mod_inputs(case, np.random.default_rng(23))
             O, lse = oracle.attention(q, k, v, scale, causal, lib=lib, **kw)
             Ob, lb = brute(q, k, v, scale, causal, **bkw)
             assert_close(O, Ob, 1e-12, "O")
