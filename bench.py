@@ -42,8 +42,24 @@ def log(*a):
 # ----------------------------------------------------------------------------
 # algorithmic work (shared with the tests that pin these formulas)
 # ----------------------------------------------------------------------------
-def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
-    """(query, key) pairs that enter the softmax for one head."""
+def visible_pairs(Lq: int, Lk: int, causal: bool, window=None) -> int:
+    """(query, key) pairs that enter the softmax for one head.  ``window`` =
+    (left, right) keeps keys p - left <= j <= p + right (negative = unbounded)
+    around each query's position p = i + Lk - Lq."""
+    if window is not None:
+        wl, wr = window
+        total = 0
+        for i in range(Lq):
+            p = i + Lk - Lq
+            lo, hi = 0, Lk - 1
+            if causal:
+                hi = min(hi, p)
+            if wl >= 0:
+                lo = max(lo, p - wl)
+            if wr >= 0:
+                hi = min(hi, p + wr)
+            total += max(0, hi - lo + 1)
+        return total
     if not causal:
         return Lq * Lk
     off = Lk - Lq
@@ -61,9 +77,9 @@ def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
     return total
 
 
-def attention_flops(B, Hq, Lq, Lk, D, causal) -> int:
+def attention_flops(B, Hq, Lq, Lk, D, causal, window=None) -> int:
     """2*D FLOP for q.k and 2*D for p*v per visible pair."""
-    return 4 * D * B * Hq * visible_pairs(Lq, Lk, causal)
+    return 4 * D * B * Hq * visible_pairs(Lq, Lk, causal, window)
 
 
 def prefill_bytes(B, Hq, Hkv, Lq, Lk, D, elem=2, o_elem=2) -> int:
@@ -136,7 +152,7 @@ def time_prefill(w, steps, warmup, warm_s=1.0):
 
     log("prefill leg: %s, generating inputs" % w.name)
     q, k, v = synth.make_qkv(w, device="cuda")
-    kw = {}
+    kw = {"softcap": w.softcap, "window": w.window}
     if w.bias == "alibi":
         kw["alibi_slopes"] = synth.alibi_slopes(w.Hq).cuda()
     o = torch.empty_like(q)
@@ -156,7 +172,7 @@ def time_prefill(w, steps, warmup, warm_s=1.0):
     wall = time.perf_counter() - t0
     durs = sorted(a.elapsed_time(b) for a, b in ev)
     avg_ms = sum(durs) / len(durs)
-    flops = attention_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal)
+    flops = attention_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal, w.window)
     log("prefill: wall %.3f ms/step, kernel avg %.4f ms (p10 %.4f, p90 %.4f)" %
         (wall * 1e3 / steps, avg_ms, durs[len(durs) // 10], durs[(9 * len(durs)) // 10]))
     del q, k, v, o, lse
@@ -229,9 +245,10 @@ def cpu_baseline(w, budget_s=15.0):
         q, k, v = synth.make_qkv(ws)
         q, k, v = q.float().numpy(), k.float().numpy(), v.float().numpy()
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, w.softmax_scale(), w.causal, threads=threads)
+        oracle.attention(q, k, v, w.softmax_scale(), w.causal, softcap=w.softcap, window=w.window,
+                         threads=threads)
         t = time.perf_counter() - t0
-        return t, attention_flops(1, n_heads * G, w.Lq, w.Lk, w.D, w.causal)
+        return t, attention_flops(1, n_heads * G, w.Lq, w.Lk, w.D, w.causal, w.window)
 
     t1, f1 = run(1)
     n = int(max(1, min(w.B * w.Hkv, round(budget_s / max(t1, 1e-3)))))
@@ -376,7 +393,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 inputs)",
         "config": {"workload": wp.name, "B": wp.B, "H": wp.Hq, "Lq": wp.Lq, "Lk": wp.Lk, "D": wp.D,
-                   "causal": wp.causal, "bias": wp.bias, "parallelism": "single GPU"},
+                   "causal": wp.causal, "bias": wp.bias, "softcap": wp.softcap,
+                   "window": list(wp.window) if wp.window else None, "parallelism": "single GPU"},
         "roofline": {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": round(p_kern_tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(p_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -101,6 +101,17 @@ typedef struct attn_fwd_args {
     void *o;                         /* device pointer, O [B, Hq, Lq, D] */
     int64_t o_strides[3];            /* b, h, l strides of o in elements */
     float *lse;                      /* device pointer to [B, Hq, Lq] fp32, or NULL */
+    /* SoftCap and Window, the two further score modifiers the Neptune notes
+       list in section 9 (named there without a formula; these are the plain
+       readings).  A zero-filled tail leaves both off. */
+    float softcap;                   /* > 0: the scaled score t = scale*<q,k> becomes
+                                        softcap * tanh(t / softcap) before the bias is added;
+                                        0 = off */
+    int32_t window;                  /* 1: only keys p - window_left <= j <= p + window_right
+                                        are visible (p = i + Lk - Lq, intersected with the
+                                        causal bound); 0 = no window */
+    int32_t window_left;             /* keys to the left of p; negative = unbounded */
+    int32_t window_right;            /* keys to the right of p; negative = unbounded */
 } attn_fwd_args;
 
 /*

@@ -51,6 +51,8 @@ class AttnFwdArgs(ctypes.Structure):
         ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
         ("bias_strides", _I64x4), ("alibi_slopes", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("o_strides", _I64x3), ("lse", ctypes.c_void_p),
+        ("softcap", ctypes.c_float), ("window", ctypes.c_int32),
+        ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
     ]
 
 
@@ -136,7 +138,8 @@ def _strides3(t: torch.Tensor):
     return _I64x3(*[int(x) for x in t.stride()[:3]])
 
 
-def _make_args(q, k, v, scale, causal, bias, alibi_slopes, o=None, lse=None) -> AttnFwdArgs:
+def _make_args(q, k, v, scale, causal, bias, alibi_slopes, o=None, lse=None, softcap=0.0,
+               window=None) -> AttnFwdArgs:
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_4d(name, t)
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -179,6 +182,10 @@ def _make_args(q, k, v, scale, causal, bias, alibi_slopes, o=None, lse=None) -> 
     else:
         a.o_dtype = a.dtype
     a.lse = _ptr(lse)
+    a.softcap = float(softcap or 0.0)
+    if window is not None:
+        a.window = 1
+        a.window_left, a.window_right = int(window[0]), int(window[1])
     return a
 
 
@@ -189,11 +196,14 @@ def attn_fwd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: O
                      causal: bool = False, *, bias: Optional[torch.Tensor] = None,
                      alibi_slopes: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                      out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
-                     return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                     return_lse: bool = True, softcap: float = 0.0,
+                     window: Optional[Tuple[int, int]] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Fused attention forward (rolling update).  q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D].
 
     Returns (O [B,Hq,Lq,D], LSE [B,Hq,Lq] fp32 or None).  ``bias`` broadcasts to
-    [B,Hq,Lq,Lk]; ``alibi_slopes`` is an fp32 [Hq] tensor.
+    [B,Hq,Lq,Lk]; ``alibi_slopes`` is an fp32 [Hq] tensor; ``softcap`` > 0 caps
+    the scaled score; ``window`` = (left, right) keys around each query's
+    position (negative = unbounded).
     """
     lib = load_library()
     B, Hq, Lq, D = q.shape
@@ -205,7 +215,7 @@ def attn_fwd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: O
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq * Lq):
         raise ValueError("lse must be a contiguous fp32 tensor of B*Hq*Lq elements")
-    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, out, lse)
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, out, lse, softcap, window)
     st = lib.attn_fwd_prefill(ctypes.byref(a), _stream(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_prefill")
@@ -222,7 +232,8 @@ def chunk_length(Lk: int, num_splits: int) -> int:
 
 
 def attn_fwd_decode_splitk(q, k, v, num_splits: int, scale: Optional[float] = None, causal: bool = False, *,
-                           bias=None, alibi_slopes=None, o_part=None, m_part=None, l_part=None):
+                           bias=None, alibi_slopes=None, o_part=None, m_part=None, l_part=None,
+                           softcap: float = 0.0, window: Optional[Tuple[int, int]] = None):
     """Split-K local step: partials (o [B,Hq,Lq,S,D], m [B,Hq,Lq,S], l [B,Hq,Lq,S]) in fp32."""
     lib = load_library()
     B, Hq, Lq, D = q.shape
@@ -238,7 +249,7 @@ def attn_fwd_decode_splitk(q, k, v, num_splits: int, scale: Optional[float] = No
                        ("l_part", l_part, B * Hq * Lq * S)):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n or not t.is_cuda:
             raise ValueError("%s must be a contiguous GPU fp32 tensor of %d elements" % (name, n))
-    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes)
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, softcap=softcap, window=window)
     st = lib.attn_fwd_decode_splitk(ctypes.byref(a), S, _ptr(o_part), _ptr(m_part), _ptr(l_part), _stream(dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_decode_splitk")
@@ -283,7 +294,8 @@ def attn_device_cu_count(device: int = 0) -> int:
 
 
 def decode(q, k, v, num_splits: Optional[int] = None, scale: Optional[float] = None, causal: bool = False, *,
-           bias=None, alibi_slopes=None, out=None, out_dtype=None, workspace=None, return_lse: bool = True):
+           bias=None, alibi_slopes=None, out=None, out_dtype=None, workspace=None, return_lse: bool = True,
+           softcap: float = 0.0, window: Optional[Tuple[int, int]] = None):
     """Split-K decode: local step then combine, both enqueued on the current stream.
 
     ``workspace`` may be a tuple (o_part, m_part, l_part) to reuse.
@@ -297,6 +309,7 @@ def decode(q, k, v, num_splits: Optional[int] = None, scale: Optional[float] = N
         o_part, m_part, l_part = workspace
     o_part, m_part, l_part = attn_fwd_decode_splitk(q, k, v, num_splits, scale, causal, bias=bias,
                                                     alibi_slopes=alibi_slopes, o_part=o_part,
-                                                    m_part=m_part, l_part=l_part)
+                                                    m_part=m_part, l_part=l_part, softcap=softcap,
+                                                    window=window)
     return attn_splitk_combine(o_part, m_part, l_part, out=out, out_dtype=out_dtype or q.dtype,
                                return_lse=return_lse)

@@ -49,6 +49,8 @@ attn_status check_common(const attn_fwd_args *a) {
         if (!aligned(a->bias, (uintptr_t)elem_size(a->bias_dtype))) return ATTN_ERR_UNSUPPORTED;
     }
     if (a->bias_kind == ATTN_BIAS_ALIBI && any_q && a->alibi_slopes == nullptr) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(a->softcap) || a->softcap < 0.f) return ATTN_ERR_INVALID_ARG;
+    if (a->window != 0 && a->window != 1) return ATTN_ERR_INVALID_ARG;
 
     // implemented shapes
     if (a->D != 64 && a->D != 128) return ATTN_ERR_UNSUPPORTED;
@@ -89,6 +91,16 @@ FwdParams make_params(const attn_fwd_args *a) {
         p.bias_kind = a->bias_dtype == ATTN_BF16 ? attn::kBiasDenseBf16 : attn::kBiasDenseF32;
     else
         p.bias_kind = attn::kBiasNone;
+    if (a->softcap > 0.f) {
+        p.bias_kind = p.bias_kind == attn::kBiasNone ? (int)attn::kBiasNoneCap : p.bias_kind + 5;
+        p.softcap = a->softcap;
+        p.cap_l2 = a->softcap * 1.4426950408889634f;
+        p.cap_k = 2.f / a->softcap;
+        p.cap_inv = 1.f / p.cap_l2;
+    }
+    p.window = a->window;
+    p.win_left = a->window_left;
+    p.win_right = a->window_right;
     return p;
 }
 

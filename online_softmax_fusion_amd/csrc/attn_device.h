@@ -42,6 +42,19 @@ __device__ __forceinline__ float xor32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Soft cap of a score x in log2 units: c * tanh(x / c) with c = cap (the cap
+// in log2 units) and k2 = 2 * log2(e) / c.  For |y| = |x / c| >= 1/16,
+// tanh(y) = 1 - 2 / (e^(2y) + 1) with e^(2y) = 2^(x * k2) (relative error a
+// few 1e-6); below that the series tanh(y) = y (1 - y^2/3 + ...) is used,
+// where the exp form would cancel (the dropped terms are < 1e-6 relative).
+__device__ __forceinline__ float soft_cap(float x, float cap, float k2, float inv_cap) {
+    const float y = x * inv_cap;
+    const float e2 = __builtin_amdgcn_exp2f(x * k2);
+    const float far = fmaf(-2.f * cap, __builtin_amdgcn_rcpf(e2 + 1.f), cap);
+    const float near = fmaf(-x * y * y, 0.33333334f, x);
+    return fabsf(y) < 0.0625f ? near : far;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

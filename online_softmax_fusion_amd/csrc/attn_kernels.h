@@ -7,8 +7,15 @@
 
 namespace attn {
 
-// kBiasNoneScaled: no bias, score formed explicitly (used when the scale is not positive)
-enum BiasKind { kBiasNone = 0, kBiasAlibi = 1, kBiasDenseF32 = 2, kBiasDenseBf16 = 3, kBiasNoneScaled = 4 };
+// kBiasNoneScaled: no bias, score formed explicitly (used when the scale is not
+// positive).  The *Cap kinds add the soft cap of the scaled score.
+enum BiasKind {
+    kBiasNone = 0, kBiasAlibi = 1, kBiasDenseF32 = 2, kBiasDenseBf16 = 3, kBiasNoneScaled = 4,
+    kBiasNoneCap = 5, kBiasAlibiCap = 6, kBiasDenseF32Cap = 7, kBiasDenseBf16Cap = 8
+};
+// the bias part of a kind, and whether it carries the soft cap
+constexpr int bias_base(int kind) { return kind == kBiasNoneCap ? kBiasNoneScaled : kind >= kBiasAlibiCap ? kind - 5 : kind; }
+constexpr bool bias_cap(int kind) { return kind >= kBiasNoneCap; }
 
 // One attention problem after validation.  Strides are in elements.
 struct FwdParams {
@@ -30,7 +37,29 @@ struct FwdParams {
     int num_splits, chunk;              // decode: number of key chunks, keys per chunk
     float scale;                        // softmax scale (natural units)
     float scale_log2;                   // scale * log2(e)
+    float softcap;                      // soft cap of the scaled score (natural units); 0 = off
+    float cap_l2;                       // soft cap in log2 units (softcap * log2(e)); 0 = off
+    float cap_k;                        // 2 / softcap: 2^(x * cap_k) = e^(2 x / cap_l2)
+    float cap_inv;                      // 1 / cap_l2
+    int window;                         // 1: apply win_left / win_right
+    int win_left, win_right;            // keys left / right of the query position; < 0 = unbounded
 };
+
+// Visible key range [jmin, jmax] of the query at end-aligned position
+// pos = i + Lk - Lq (so pos <= Lk - 1): causal bound, window bounds, keys that
+// exist.  jmax < jmin means no visible key (only for pos < 0).  Both ends are
+// non-decreasing in pos, so the rows of a tile see the keys between the
+// first row's jmin and the last row's jmax.
+__host__ __device__ inline void key_range(const FwdParams &p, int pos, int &jmin, int &jmax) {
+    int64_t lo = 0, hi = (int64_t)p.Lk - 1;
+    if (p.causal && pos < hi) hi = pos;
+    if (p.window) {
+        if (p.win_left >= 0 && (int64_t)pos - p.win_left > lo) lo = (int64_t)pos - p.win_left;
+        if (p.win_right >= 0 && (int64_t)pos + p.win_right < hi) hi = (int64_t)pos + p.win_right;
+    }
+    jmin = (int)lo;
+    jmax = (int)hi;
+}
 
 struct CombineParams {
     const float *o_part, *m_part, *l_part;

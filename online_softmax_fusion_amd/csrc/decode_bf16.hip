@@ -116,8 +116,10 @@ template <int D, int BIAS>
 __device__ __forceinline__ void decode_block(const FwdParams &p, const char *lk, const char *lv, int kbase,
                                              int vbase, const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32],
                                              float &m_run, float &l_run, int kb0, int k_hi, int qi, int qpos,
-                                             float slope_l2, int b, int h, int lane) {
+                                             int jmin, int jmax, float slope_l2, int b, int h, int lane) {
     using C = BlockCfg<D>;
+    constexpr int BK = bias_base(BIAS);
+    constexpr bool CAP = bias_cap(BIAS);
     const int hh = lane >> 5;
 
     // S^T = K Q^T: two accumulation chains over the k-steps
@@ -129,27 +131,28 @@ __device__ __forceinline__ void decode_block(const FwdParams &p, const char *lk,
         s0 = mfma32(as_bf16x8(load16(lk + (kbase ^ (ks << 5)))), as_bf16x8(qreg[ks]), s0);
         s1 = mfma32(as_bf16x8(load16(lk + (kbase ^ ((ks + 1) << 5)))), as_bf16x8(qreg[ks + 1]), s1);
     }
-    const bool need_mask = (kb0 + C::BK > k_hi) || p.causal;
+    const bool need_mask = (kb0 + C::BK > k_hi) || p.causal || p.window;
     float mx = -INFINITY;
     f32x16 sc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int j = kb0 + (e >> 3) * 16 + hh * 8 + (e & 7);
         float x = (s0[e] + s1[e]) * p.scale_log2;
-        if (BIAS == kBiasAlibi) {
+        if (CAP) x = soft_cap(x, p.cap_l2, p.cap_k, p.cap_inv);   // in log2 units
+        if (BK == kBiasAlibi) {
             x -= slope_l2 * fabsf((float)(qpos - j));
-        } else if (BIAS == kBiasDenseF32 || BIAS == kBiasDenseBf16) {
+        } else if (BK == kBiasDenseF32 || BK == kBiasDenseBf16) {
             const int bj = min(j, p.Lk - 1);
             const int64_t idx = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh + (int64_t)qi * p.bias_si +
                                 (int64_t)bj * p.bias_sj;
             float bv;
-            if (BIAS == kBiasDenseF32)
+            if (BK == kBiasDenseF32)
                 bv = static_cast<const float *>(p.bias)[idx];
             else
                 bv = bf16_bits_to_f32(static_cast<const uint16_t *>(p.bias)[idx]);
             x = fmaf(bv, kLog2e, x);
         }
-        if (need_mask && (j >= k_hi || (p.causal && j > qpos))) x = -INFINITY;
+        if (need_mask && (j >= k_hi || j < jmin || j > jmax)) x = -INFINITY;
         sc[e] = x;
         mx = fmaxf(mx, x);
     }
@@ -244,9 +247,16 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(FwdParams p) {
     const int qi = rho_c - g * p.Lq;
     const int h = hk * p.G + g;
     const int qpos = qi + off;
+    int jmin, jmax;
+    key_range(p, qpos, jmin, jmax);
 
-    const int k_lo = s * p.chunk;
-    const int k_hi = min(k_lo + p.chunk, p.Lk);
+    // the chunk's keys, narrowed to those some query row of the group can see
+    // (rows of all Lq positions share a workgroup, so take the first and last)
+    int gjmin, gjmax, unused;
+    key_range(p, off, gjmin, unused);
+    key_range(p, p.Lq - 1 + off, unused, gjmax);
+    const int k_lo = max(s * p.chunk, gjmin);
+    const int k_hi = min(min(s * p.chunk + p.chunk, p.Lk), gjmax + 1);
     const int nblk = (k_hi > k_lo) ? (k_hi - k_lo + C::BK - 1) / C::BK : 0;
     const int nmine = (wave < nblk) ? (nblk - wave + NW - 1) / NW : 0;
 
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(FwdParams p) {
         for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = load16(qr + ks * 16);
     }
     float slope_l2 = 0.f;
-    if (BIAS == kBiasAlibi) slope_l2 = p.slopes[h] * kLog2e;
+    if (bias_base(BIAS) == kBiasAlibi) slope_l2 = p.slopes[h] * kLog2e;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) asm volatile("" : "+v"(qreg[ks]));
     asm volatile("" : "+v"(slope_l2));
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(NW * 64) void decode_bf16_kernel(FwdParams p) {
         wait_blocks<NLB, NST>(min(NST - 1, nmine - 1 - n_));                                                     \
         const int kb0 = k_lo + (wave + n_ * NW) * C::BK;                                                         \
         decode_block<D, BIAS>(p, (STG_)[wave], (STG_)[wave] + C::TB, kbase, vbase, qreg, oacc, m_run, l_run,     \
-                              kb0, k_hi, qi, qpos, slope_l2, b, h, lane);                                        \
+                              kb0, k_hi, qi, qpos, jmin, jmax, slope_l2, b, h, lane);                                        \
         if (n_ + NST < nmine) DEC_ISSUE(STG_, kb0 + NST * NW * C::BK);                                           \
     } while (0)
     for (int n = 0; n < nmine; n += NST) {
@@ -409,6 +419,10 @@ hipError_t launch_decode_d(const FwdParams &p, hipStream_t stream) {
         case kBiasAlibi: return launch_decode_t<D, kBiasAlibi>(p, stream);
         case kBiasDenseF32: return launch_decode_t<D, kBiasDenseF32>(p, stream);
         case kBiasDenseBf16: return launch_decode_t<D, kBiasDenseBf16>(p, stream);
+        case kBiasNoneCap: return launch_decode_t<D, kBiasNoneCap>(p, stream);
+        case kBiasAlibiCap: return launch_decode_t<D, kBiasAlibiCap>(p, stream);
+        case kBiasDenseF32Cap: return launch_decode_t<D, kBiasDenseF32Cap>(p, stream);
+        case kBiasDenseBf16Cap: return launch_decode_t<D, kBiasDenseBf16Cap>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -92,9 +92,11 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                                              int kbase, int vbase,
                                              const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32],
                                              float &m_run, float &l_run, int kt0, int qrow, int qpos,
-                                             float slope_l2, int b, int h, int lane) {
+                                             int jmin, int jmax, float slope_l2, int b, int h, int lane) {
     using C = TileCfg<D>;
     constexpr bool FOLD = (BIAS == kBiasNone);
+    constexpr int BK = bias_base(BIAS);
+    constexpr bool CAP = bias_cap(BIAS);
     const int hh = lane >> 5;
 
     // 1. S^T = K Q^T, the two 32-key blocks interleaved (two accumulation
@@ -110,14 +112,17 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
         for (int kb = 0; kb < 2; ++kb)
             s[kb] = mfma32(as_bf16x8(load16(lk + ((kbase ^ (ks << 5)) + kb * 32 * C::RB))), as_bf16x8(qreg[ks]), s[kb]);
     // schedule: operand reads ahead of the matrix core (all of them for D = 64)
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    constexpr int RA = 8;
+    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
 #pragma unroll
     for (int i = 0; i < 2 * C::KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 2 * C::KS - 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < 2 * C::KS - RA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     // 2. score modifier; tile max (raw scores when the scale is folded)
     const float sc = p.scale_log2;
+    // ALiBi distance qpos - j = dbase - (a compile-time offset of the element)
+    const float dbase = (float)(qpos - kt0 - hh * 8);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -127,22 +132,23 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
             float x = s[kb][e];
             if (!FOLD) {
                 x *= sc;
-                if (BIAS == kBiasAlibi) {
-                    x -= slope_l2 * fabsf((float)(qpos - j));
-                } else if (BIAS == kBiasDenseF32 || BIAS == kBiasDenseBf16) {
+                if (CAP) x = soft_cap(x, p.cap_l2, p.cap_k, p.cap_inv);   // in log2 units
+                if (BK == kBiasAlibi) {
+                    x = fmaf(-slope_l2, fabsf(dbase - (float)(kb * 32 + (e >> 3) * 16 + (e & 7))), x);
+                } else if (BK == kBiasDenseF32 || BK == kBiasDenseBf16) {
                     const int bi = min(qrow, p.Lq - 1);
                     const int bj = min(j, p.Lk - 1);
                     const int64_t idx = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
                                         (int64_t)bi * p.bias_si + (int64_t)bj * p.bias_sj;
                     float bv;
-                    if (BIAS == kBiasDenseF32)
+                    if (BK == kBiasDenseF32)
                         bv = static_cast<const float *>(p.bias)[idx];
                     else
                         bv = bf16_bits_to_f32(static_cast<const uint16_t *>(p.bias)[idx]);
                     x = fmaf(bv, kLog2e, x);
                 }
             }
-            if (MASK && (j >= p.Lk || (p.causal && j > qpos))) x = -INFINITY;
+            if (MASK && (j < jmin || j > jmax)) x = -INFINITY;
             s[kb][e] = x;
             mx = fmaxf(mx, x);
         }
@@ -214,11 +220,11 @@ template <int D, int BIAS, bool MASK>
 __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, const char *lv,
                                           int kbase, int vbase,
                                           const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float &m_run,
-                                          float &l_run, int kt0, int wrow0, int wrow1, int off, int qrow, int qpos,
-                                          float slope_l2, int b, int h, int lane) {
-    if (MASK && !((wrow0 < p.Lq) && (!p.causal || kt0 <= wrow1 + off))) return;
-    process_tile<D, BIAS, MASK>(p, lk, lv, kbase, vbase, qreg, oacc, m_run, l_run, kt0, qrow, qpos, slope_l2, b, h,
-                                lane);
+                                          float &l_run, int kt0, int wrow0, int wjmin, int wjmax, int qrow, int qpos,
+                                          int jmin, int jmax, float slope_l2, int b, int h, int lane) {
+    if (MASK && !((wrow0 < p.Lq) && kt0 <= wjmax && kt0 + TileCfg<D>::BC - 1 >= wjmin)) return;
+    process_tile<D, BIAS, MASK>(p, lk, lv, kbase, vbase, qreg, oacc, m_run, l_run, kt0, qrow, qpos, jmin, jmax,
+                                slope_l2, b, h, lane);
 }
 
 // Direct global->LDS loads of K/V tile T_ into the LDS tile arrays KOFF_ /
@@ -290,11 +296,24 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     const int qpos = qrow + off;
     const int wrow0 = q0 + wave * 32;
     const int wrow1 = min(wrow0 + 31, p.Lq - 1);
-
-    int kv_end = p.Lk;
-    if (p.causal) kv_end = min(p.Lk, min(q0 + BR, p.Lq) + off);
-    if (kv_end < 0) kv_end = 0;
-    const int ntiles = (kv_end + BC - 1) / BC;
+    // visible keys: this lane's row, this wave's rows, the workgroup's rows
+    int jmin, jmax, wjmin, wjmax, unused;
+    key_range(p, qpos, jmin, jmax);
+    key_range(p, wrow0 + off, wjmin, unused);
+    key_range(p, wrow1 + off, unused, wjmax);
+    const int rlast = min(q0 + BR, p.Lq) - 1;
+    int gjmin0, gjmax0, gjmin1, gjmax1;
+    key_range(p, q0 + off, gjmin0, gjmax0);
+    key_range(p, rlast + off, gjmin1, gjmax1);
+    // tiles [t_first, t_end) hold every key some row sees; tiles
+    // [u_first, u_end) are visible in full to every row (no mask)
+    int t_first = 0, t_end = 0;
+    if (rlast >= q0 && gjmax1 >= gjmin0) {
+        t_first = gjmin0 / BC;
+        t_end = gjmax1 / BC + 1;
+    }
+    const int u_first = max(t_first, (gjmin1 + BC - 1) / BC);
+    const int u_end = min(t_end, gjmax0 >= 0 ? (gjmax0 + 1) / BC : 0);
 
     const uint16_t *qp = static_cast<const uint16_t *>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
     const uint16_t *kp = static_cast<const uint16_t *>(p.k) + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
@@ -311,7 +330,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     }
 
     float slope_l2 = 0.f;
-    if (BIAS == kBiasAlibi) slope_l2 = p.slopes[h] * kLog2e;
+    if (bias_base(BIAS) == kBiasAlibi) slope_l2 = p.slopes[h] * kLog2e;
 
     // per-lane LDS byte offsets: K operand of k-step ks at kbase ^ (ks << 5)
     // (+32 rows per key block); V transposing read of d-block db at
@@ -350,50 +369,54 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
     float l_run = 0.f;         // running sum over this lane's half of the keys
 
 
-    if (ntiles > 0) {
-        ATTN_ISSUE_TILE_LOADS(0, lds_k0, lds_v0);
+    if (t_end > t_first) {
+        ATTN_ISSUE_TILE_LOADS(t_first, lds_k0, lds_v0);
         wait_vmem();
         __syncthreads();
     }
 
-    // Tiles [0, n_full) need no mask for any row of the workgroup: they run
-    // two per trip so that each LDS buffer's address is a constant.  The rest
-    // (the causal diagonal band and the key tail) take the masked path.
-    int n_full = p.Lk / BC;
-    if (p.causal) n_full = min(n_full, max(0, (q0 + off + 1) / BC));
-    n_full = min(n_full, ntiles);
+    // Tile t sits in buffer (t - t_first) & 1.  Masked tiles (the window's
+    // left edge, the causal diagonal band, the key tail) take the generic
+    // step; the unmasked middle runs two tiles per trip so that each LDS
+    // buffer's address is a constant.
 #define ATTN_STEP(MASK_, BUF_, T_)                                                                               \
     tile_step<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, kbase, vbase, qreg, oacc,    \
-                              m_run, l_run, (T_) * BC, wrow0, wrow1, off, qrow, qpos, slope_l2, b, h, lane)
-    int t = 0;
-    for (; t + 1 < n_full; t += 2) {
+                              m_run, l_run, (T_) * BC, wrow0, wjmin, wjmax, qrow, qpos, jmin, jmax, slope_l2, b, h, \
+                              lane)
+#define ATTN_GENERIC_STEP(T_)                                                                                   \
+    do {                                                                                                        \
+        const int tg_ = (T_);                                                                                   \
+        const bool masked_ = tg_ < u_first || tg_ >= u_end;                                                     \
+        if (((tg_ - t_first) & 1) == 0) {                                                                       \
+            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k1, lds_v1);                                \
+            if (masked_)                                                                                        \
+                ATTN_STEP(true, 0, tg_);                                                                        \
+            else                                                                                                \
+                ATTN_STEP(false, 0, tg_);                                                                       \
+        } else {                                                                                                \
+            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k0, lds_v0);                                \
+            if (masked_)                                                                                        \
+                ATTN_STEP(true, 1, tg_);                                                                        \
+            else                                                                                                \
+                ATTN_STEP(false, 1, tg_);                                                                       \
+        }                                                                                                       \
+        wait_vmem();                                                                                            \
+        __syncthreads();                                                                                        \
+    } while (0)
+    int t = t_first;
+    for (; t < t_end && !(t >= u_first && ((t - t_first) & 1) == 0); ++t) ATTN_GENERIC_STEP(t);
+    for (; t + 1 < u_end; t += 2) {
         ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1);
         ATTN_STEP(false, 0, t);
         wait_vmem();
         __syncthreads();
-        if (t + 2 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 2, lds_k0, lds_v0);
+        if (t + 2 < t_end) ATTN_ISSUE_TILE_LOADS(t + 2, lds_k0, lds_v0);
         ATTN_STEP(false, 1, t + 1);
         wait_vmem();
         __syncthreads();
     }
-    for (; t < ntiles; ++t) {
-        const bool masked = t >= n_full;
-        if ((t & 1) == 0) {
-            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1);
-            if (masked)
-                ATTN_STEP(true, 0, t);
-            else
-                ATTN_STEP(false, 0, t);
-        } else {
-            if (t + 1 < ntiles) ATTN_ISSUE_TILE_LOADS(t + 1, lds_k0, lds_v0);
-            if (masked)
-                ATTN_STEP(true, 1, t);
-            else
-                ATTN_STEP(false, 1, t);
-        }
-        wait_vmem();
-        __syncthreads();
-    }
+    for (; t < t_end; ++t) ATTN_GENERIC_STEP(t);
+#undef ATTN_GENERIC_STEP
 #undef ATTN_STEP
 
     // epilogue
@@ -450,6 +473,10 @@ hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
         case kBiasAlibi: return launch_prefill_t<D, NW, kBiasAlibi>(p, stream);
         case kBiasDenseF32: return launch_prefill_t<D, NW, kBiasDenseF32>(p, stream);
         case kBiasDenseBf16: return launch_prefill_t<D, NW, kBiasDenseBf16>(p, stream);
+        case kBiasNoneCap: return launch_prefill_t<D, NW, kBiasNoneCap>(p, stream);
+        case kBiasAlibiCap: return launch_prefill_t<D, NW, kBiasAlibiCap>(p, stream);
+        case kBiasDenseF32Cap: return launch_prefill_t<D, NW, kBiasDenseF32Cap>(p, stream);
+        case kBiasDenseBf16Cap: return launch_prefill_t<D, NW, kBiasDenseBf16Cap>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -49,7 +49,10 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(FwdParams p) {
         k_lo = s * p.chunk;
         k_hi = min(k_lo + p.chunk, p.Lk);
     }
-    if (p.causal) k_hi = min(k_hi, qpos + 1);
+    int jmin, jmax;   // causal and window bounds
+    key_range(p, qpos, jmin, jmax);
+    k_lo = max(k_lo, jmin);
+    k_hi = min(k_hi, jmax + 1);
 
     const float *qr = static_cast<const float *>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)i * p.q_sl;
     const float *kp = static_cast<const float *>(p.k) + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
@@ -81,6 +84,7 @@ __global__ __launch_bounds__(64) void rows_f32_kernel(FwdParams p) {
                 dot = fmaf(qv[3], kv[3], dot);
             }
             x = dot * p.scale;
+            if (p.softcap > 0.f) x = p.softcap * tanhf(x / p.softcap);
             if (BIAS == kBiasAlibi) {
                 x -= slope * fabsf((float)(qpos - j));
             } else if (BIAS == kBiasDenseF32) {
@@ -139,7 +143,9 @@ hipError_t launch_rows_t(const FwdParams &p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
     if (rows == 0) return hipSuccess;
     dim3 grid((unsigned)rows, PARTIAL ? (unsigned)p.num_splits : 1u), block(64);
-    switch (p.bias_kind) {
+    // the soft cap is a run-time branch here (this path is not bound by the vector units)
+    switch (bias_base(p.bias_kind)) {
+        case kBiasNoneScaled:
         case kBiasNone: hipLaunchKernelGGL((rows_f32_kernel<D, kBiasNone, PARTIAL>), grid, block, 0, stream, p); break;
         case kBiasAlibi: hipLaunchKernelGGL((rows_f32_kernel<D, kBiasAlibi, PARTIAL>), grid, block, 0, stream, p); break;
         case kBiasDenseF32: hipLaunchKernelGGL((rows_f32_kernel<D, kBiasDenseF32, PARTIAL>), grid, block, 0, stream, p); break;

@@ -47,6 +47,8 @@ class Workload:
     seed: int = 0
     scale: Optional[float] = None  # None -> 1/sqrt(D) rounded to fp32
     splits: Optional[int] = None   # decode only: number of KV chunks
+    softcap: float = 0.0           # > 0: cap of the scaled score
+    window: Optional[tuple] = None  # (left, right) keys around each query's position
     extra: dict = field(default_factory=dict, compare=False)
 
     def softmax_scale(self) -> float:
@@ -70,7 +72,17 @@ C5_PREFILL = Workload("long-causal-prefill-bf16-B1-H8-L32768-d128", 1, 8, 8, 327
 C5_DECODE = Workload("long-decode-bf16-B1-H8-Lk32768-d128", 1, 8, 8, 1, 32768, 128,
                      "bf16", False, "none", 1005)
 
-WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PREFILL, C5_DECODE)}
+# The next score modifiers (SoftCap and Window of the Neptune notes, section 9),
+# on shapes of the workloads above: a Gemma-style cap of 50 on the causal
+# B4 H32 L4096 prefill, and a causal sliding window of 4096 keys (the query's
+# own key and 4095 before it) on the long B1 H8 L32768 prefill.
+SOFTCAP_PREFILL = Workload("softcap50-causal-prefill-bf16-B4-H32-L4096-d128", 4, 32, 32, 4096, 4096, 128,
+                           "bf16", True, "none", 1006, softcap=50.0)
+WINDOW_PREFILL = Workload("window4096-causal-prefill-bf16-B1-H8-L32768-d128", 1, 8, 8, 32768, 32768, 128,
+                          "bf16", True, "none", 1007, window=(4095, -1))
+
+WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PREFILL, C5_DECODE,
+                                 SOFTCAP_PREFILL, WINDOW_PREFILL)}
 
 
 def torch_dtype(name: str) -> torch.dtype:

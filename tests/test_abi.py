@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_struct_layout_matches(lib):
-    assert lib.attn_fwd_args_size() == ctypes.sizeof(attn.AttnFwdArgs) == 256
+    assert lib.attn_fwd_args_size() == ctypes.sizeof(attn.AttnFwdArgs) == 272
 
 
 def test_status_strings(lib):
@@ -88,6 +88,10 @@ def test_valid_args_pass(lib):
     (lambda a: setattr(a, "bias_kind", attn.ATTN_BIAS_DENSE), INVALID),   # null bias
     (lambda a: setattr(a, "bias_kind", attn.ATTN_BIAS_ALIBI), INVALID),   # null slopes
     (lambda a: a.k_strides.__setitem__(2, -128), INVALID),
+    (lambda a: setattr(a, "softcap", -1.0), INVALID),
+    (lambda a: setattr(a, "softcap", float("nan")), INVALID),
+    (lambda a: setattr(a, "softcap", float("inf")), INVALID),
+    (lambda a: setattr(a, "window", 2), INVALID),
     (lambda a: setattr(a, "D", 96), UNSUPPORTED),
     (lambda a: setattr(a, "D", 256), UNSUPPORTED),
     (lambda a: setattr(a, "q", P1 + 2), UNSUPPORTED),     # misaligned

@@ -26,6 +26,22 @@ def test_visible_pairs_brute(Lq, Lk):
     assert bench.visible_pairs(Lq, Lk, False) == Lq * Lk
 
 
+@pytest.mark.parametrize("Lq,Lk,causal,window", [
+    (9, 9, True, (3, -1)), (7, 12, False, (2, 4)), (12, 7, True, (0, 0)), (10, 10, False, (-1, 2)),
+    (5, 20, True, (100, 100)), (64, 64, True, (15, -1)), (3, 40, False, (5, -1))])
+def test_visible_pairs_window_brute(Lq, Lk, causal, window):
+    pos = np.arange(Lq)[:, None] + (Lk - Lq)
+    keys = np.arange(Lk)[None, :]
+    vis = np.ones((Lq, Lk), bool)
+    if causal:
+        vis &= keys <= pos
+    if window[0] >= 0:
+        vis &= keys >= pos - window[0]
+    if window[1] >= 0:
+        vis &= keys <= pos + window[1]
+    assert bench.visible_pairs(Lq, Lk, causal, window) == int(vis.sum())
+
+
 def test_head_matmul_flops(numbers):
     h = numbers["head"]
     f = bench.attention_flops(1, 1, h["N"], h["N"], h["d"], False)

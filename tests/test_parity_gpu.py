@@ -92,6 +92,71 @@ def test_prefill_parity(case):
     compare(o, lse, O_ref, L_ref, dtype, str(case))
 
 
+# SoftCap and sliding Window (the readings of the oracle: cap on the scaled
+# score before the bias; keys p - left <= j <= p + right, negative = unbounded)
+MOD_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, softcap, window
+    (1, 4, 4, 300, 300, 128, "bf16", True, "none", 0.0, (64, -1)),     # causal sliding window
+    (1, 2, 2, 200, 333, 128, "bf16", True, "none", 0.0, (100, 0)),     # Lq < Lk
+    (2, 2, 1, 257, 257, 128, "bf16", False, "none", 0.0, (70, 30)),    # two-sided, unaligned
+    (1, 2, 2, 260, 260, 64, "bf16", True, "none", 0.0, (0, 0)),        # only the diagonal
+    (1, 2, 2, 300, 150, 128, "bf16", True, "none", 0.0, (40, -1)),     # Lq > Lk: empty rows
+    (1, 2, 2, 190, 190, 128, "bf16", False, "none", 0.0, (-1, 5)),     # right bound only
+    (1, 4, 4, 256, 256, 128, "bf16", True, "none", 2.0, None),         # soft cap
+    (2, 2, 2, 130, 190, 128, "bf16", False, "alibi", 5.0, None),       # cap + ALiBi
+    (1, 2, 2, 129, 129, 64, "bf16", True, "dense_bf16", 3.0, (20, -1)),  # cap + bias + window
+    (1, 2, 2, 160, 160, 128, "bf16", True, "none", 30.0, (50, -1)),    # loose cap + window
+    (1, 2, 2, 150, 333, 128, "f32", True, "none", 4.0, (60, -1)),      # fp32 path
+    (1, 2, 2, 97, 200, 64, "f32", False, "alibi", 1.5, (10, 10)),
+]
+
+
+@pytest.mark.parametrize("case", MOD_CASES, ids=[str(i) for i in range(len(MOD_CASES))])
+def test_prefill_softcap_window_parity(case):
+    B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, softcap, window = case
+    w, q, k, v, gkw, okw = inputs(B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, seed=61 + Lq, qk_scale=2.0)
+    print("prefill softcap/window case", case, flush=True)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), causal, softcap=softcap,
+                                   window=window, **gkw)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, softcap=softcap, window=window, **okw)
+    compare(o, lse, O_ref, L_ref, dtype, str(case))
+
+
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, softcap, window, splits
+    (2, 8, 2, 1, 1000, 128, "bf16", False, "none", 0.0, (300, -1), 4),   # chunks outside the window
+    (1, 4, 4, 1, 777, 128, "bf16", True, "none", 3.0, (100, 0), 3),
+    (1, 16, 2, 5, 700, 128, "bf16", True, "alibi", 5.0, (64, -1), 6),  # 40 stacked rows
+    (2, 4, 2, 1, 300, 64, "bf16", False, "dense_f32", 2.0, None, 3),
+    (1, 4, 2, 1, 500, 128, "f32", False, "none", 4.0, (50, -1), 4),
+    (1, 2, 2, 3, 300, 64, "f32", True, "alibi", 0.0, (0, 0), 2),
+], ids=[str(i) for i in range(6)])
+def test_decode_softcap_window_parity(case):
+    B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, softcap, window, S = case
+    w, q, k, v, gkw, okw = inputs(B, Hq, Hkv, Lq, Lk, D, dtype, causal, bias, seed=91 + S, qk_scale=2.0)
+    print("decode softcap/window case", case, flush=True)
+    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), S, w.softmax_scale(), causal, softcap=softcap,
+                         window=window, out_dtype=torch.float32, **gkw)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, softcap=softcap, window=window, **okw)
+    compare(o, lse, O_ref, L_ref, dtype, str(case))
+
+
+def test_unbounded_window_and_huge_cap_match_plain():
+    """A window wider than the keys and a cap far above every score give the
+    plain kernel's result (up to the cap's rounding)."""
+    w, q, k, v, _, _ = inputs(1, 4, 4, 200, 200, 128, "bf16", True, seed=5)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    o0, l0 = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), True)
+    o1, l1 = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), True, window=(1000, 1000))
+    o2, l2 = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), True, softcap=1e6)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert float((o2.float() - o0.float()).abs().max()) <= 1.6e-2
+    assert float((l2 - l0).abs().max()) <= 1e-3
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_fp32_output(dtype):
     w, q, k, v, _, _ = inputs(1, 2, 2, 140, 140, 128, dtype, True)
