@@ -50,6 +50,10 @@ def load_path(path: str):
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_splitk_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_splitk_combine.restype = ctypes.c_int
+    lib.oracle_attention_bwd.argtypes = [i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, dbl, ctypes.c_int,
+                                         dbl, ctypes.c_int, i64, i64,
+                                         ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -75,26 +79,9 @@ def default_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-def attention(q, k, v, scale: float, causal: bool = False, *, bias=None,
-              alibi_slopes=None, softcap: float = 0.0, window: Optional[Sequence[int]] = None,
-              rows: Optional[Sequence[int]] = None, threads: Optional[int] = None, lib=None):
-    """fp64 O [rows, D] and LSE [rows] of attention over q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D].
-
-    ``bias`` is an additive score bias broadcastable to [B, Hq, Lq, Lk] (numpy or
-    torch; size-1 dims broadcast).  ``alibi_slopes`` [Hq] selects the ALiBi bias
-    -slope[h] * |i + Lk - Lq - j| instead.  ``softcap`` > 0 bounds the scaled
-    score to softcap * tanh(score / softcap) before the bias.  ``window`` =
-    (left, right) keeps only keys j with p - left <= j <= p + right, p = i + Lk
-    - Lq (a negative bound is unbounded).  ``rows`` selects flat row ids
-    (b*Hq + h)*Lq + i; by default every row is returned, in order, and O is
-    reshaped to [B, Hq, Lq, D] and LSE to [B, Hq, Lq].
-    """
-    lib = lib or load()
-    qa, ka, va = _f32(q), _f32(k), _f32(v)
-    B, Hq, Lq, D = qa.shape
-    Bk, Hkv, Lk, Dk = ka.shape
-    if va.shape != ka.shape or Bk != B or Dk != D:
-        raise ValueError("shape mismatch between q, k and v")
+def _bias_args(bias, alibi_slopes, B, Hq, Lq, Lk):
+    """(kind, bias array, element strides, slopes) for the C oracle; a dense bias
+    broadcasts to [B, Hq, Lq, Lk] through zero strides."""
     kind, ba, strides, sa = BIAS_NONE, None, None, None
     if bias is not None and alibi_slopes is not None:
         raise ValueError("give either a dense bias or ALiBi slopes, not both")
@@ -120,6 +107,30 @@ def attention(q, k, v, scale: float, causal: bool = False, *, bias=None,
         if sa.shape[0] != Hq:
             raise ValueError("need one ALiBi slope per query head")
         kind = BIAS_ALIBI
+    return kind, ba, strides, sa
+
+
+def attention(q, k, v, scale: float, causal: bool = False, *, bias=None,
+              alibi_slopes=None, softcap: float = 0.0, window: Optional[Sequence[int]] = None,
+              rows: Optional[Sequence[int]] = None, threads: Optional[int] = None, lib=None):
+    """fp64 O [rows, D] and LSE [rows] of attention over q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D].
+
+    ``bias`` is an additive score bias broadcastable to [B, Hq, Lq, Lk] (numpy or
+    torch; size-1 dims broadcast).  ``alibi_slopes`` [Hq] selects the ALiBi bias
+    -slope[h] * |i + Lk - Lq - j| instead.  ``softcap`` > 0 bounds the scaled
+    score to softcap * tanh(score / softcap) before the bias.  ``window`` =
+    (left, right) keeps only keys j with p - left <= j <= p + right, p = i + Lk
+    - Lq (a negative bound is unbounded).  ``rows`` selects flat row ids
+    (b*Hq + h)*Lq + i; by default every row is returned, in order, and O is
+    reshaped to [B, Hq, Lq, D] and LSE to [B, Hq, Lq].
+    """
+    lib = lib or load()
+    qa, ka, va = _f32(q), _f32(k), _f32(v)
+    B, Hq, Lq, D = qa.shape
+    Bk, Hkv, Lk, Dk = ka.shape
+    if va.shape != ka.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k and v")
+    kind, ba, strides, sa = _bias_args(bias, alibi_slopes, B, Hq, Lq, Lk)
     ra = None
     if rows is not None:
         ra = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
@@ -157,3 +168,30 @@ def splitk_combine(o_part, m_part, l_part, lib=None):
     if rc != 0:
         raise ValueError("oracle_splitk_combine rejected its arguments (rc=%d)" % rc)
     return o.reshape(tuple(lead) + (D,)), lse.reshape(lead)
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool = False, *, bias=None, alibi_slopes=None,
+                  softcap: float = 0.0, window: Optional[Sequence[int]] = None,
+                  threads: Optional[int] = None, lib=None):
+    """fp64 (dQ [B,Hq,Lq,D], dK [B,Hkv,Lk,D], dV [B,Hkv,Lk,D]) of attention for the
+    output gradient ``dout``; the other arguments as for ``attention``."""
+    lib = lib or load()
+    qa, ka, va, da = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, Hq, Lq, D = qa.shape
+    Bk, Hkv, Lk, Dk = ka.shape
+    if va.shape != ka.shape or Bk != B or Dk != D or da.shape != qa.shape:
+        raise ValueError("shape mismatch between q, k, v and dout")
+    kind, ba, strides, sa = _bias_args(bias, alibi_slopes, B, Hq, Lq, Lk)
+    dq = np.zeros((B, Hq, Lq, D), dtype=np.float64)
+    dk = np.zeros((B, Hkv, Lk, D), dtype=np.float64)
+    dv = np.zeros((B, Hkv, Lk, D), dtype=np.float64)
+    rc = lib.oracle_attention_bwd(B, Hq, Hkv, Lq, Lk, D, _ptr(qa), _ptr(ka), _ptr(va), _ptr(da),
+                                  float(scale), int(bool(causal)), float(softcap),
+                                  0 if window is None else 1,
+                                  -1 if window is None else int(window[0]),
+                                  -1 if window is None else int(window[1]),
+                                  kind, _ptr(ba), _ptr(strides), _ptr(sa),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_attention_bwd rejected its arguments (rc=%d)" % rc)
+    return dq, dk, dv

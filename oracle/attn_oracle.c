@@ -1,6 +1,7 @@
 /*
  * attn_oracle.c -- plain fp64 reference for fused scaled-dot-product attention
- * forward (prefill and split-K decode) and for the split-K log-sum-exp combine.
+ * forward (prefill and split-K decode), for the split-K log-sum-exp combine and
+ * for the gradients of the forward (dQ, dK, dV).
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
  * CPU-baseline leg load this library.  It shares no code, header, table or
@@ -13,6 +14,8 @@
  *                    '偷懒'的数学" (ai6s.net)
  *   [Mirage lecture] CMU 15-779 Lecture 11, "Advanced ML Compilation: ML
  *                    Superoptimization (Mirage)" (semidirectx.com)
+ *   [Twill review]   "Optimal Software Pipelining and Warp Specialization for
+ *                    Tensor Core GPUs" (xllm-io.github.io paper review)
  *
  * What is computed is the plain definition, not the fused algorithm.  Both the
  * rolling update and the split-K update reach this result exactly in real
@@ -85,6 +88,50 @@ typedef struct {
     pthread_mutex_t lock;
 } oracle_job;
 
+/* The visible keys of the query at position p form one interval [jlo, jhi). */
+static void visible_keys(const oracle_job *J, int64_t p, int64_t *jlo_out, int64_t *jhi_out)
+{
+    int64_t jlo = 0, jhi = J->Lk;
+    if (J->causal && p + 1 < jhi) jhi = p + 1;
+    if (J->window) {
+        if (J->window_left >= 0 && p - J->window_left > jlo) jlo = p - J->window_left;
+        if (J->window_right >= 0 && p + J->window_right + 1 < jhi) jhi = p + J->window_right + 1;
+    }
+    *jlo_out = jlo;
+    *jhi_out = jhi;
+}
+
+/* Scores s[j - jlo] of row (b, h, i) for the keys jlo <= j < jhi of kbase.
+ * With dcap != 0, dcap[j - jlo] receives the derivative of the score with
+ * respect to the scaled product (the soft cap's slope; 1 without a cap). */
+static void row_scores(const oracle_job *J, int64_t b, int64_t h, int64_t i, int64_t p,
+                       int64_t jlo, int64_t jhi, const float *qrow, const float *kbase,
+                       double *s, double *dcap)
+{
+    const int64_t D = J->D;
+    for (int64_t j = jlo; j < jhi; ++j) {
+        const float *krow = kbase + j * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (double)krow[d];
+        double sj = J->scale * dot, slope = 1.0;
+        if (J->softcap > 0.0) {
+            const double th = tanh(sj / J->softcap);
+            sj = J->softcap * th;
+            slope = 1.0 - th * th;
+        }
+        if (J->bias_kind == ORACLE_BIAS_DENSE) {
+            const int64_t *st = J->bias_strides;
+            sj += (double)J->bias[b * st[0] + h * st[1] + i * st[2] + j * st[3]];
+        } else if (J->bias_kind == ORACLE_BIAS_ALIBI) {
+            double dist = (double)(p - j);
+            if (dist < 0) dist = -dist;
+            sj += -(double)J->slopes[h] * dist;
+        }
+        s[j - jlo] = sj;
+        if (dcap) dcap[j - jlo] = slope;
+    }
+}
+
 /* One output row, two passes over its visible keys. */
 static void oracle_row(const oracle_job *J, int64_t flat, double *o, double *lse, double *s)
 {
@@ -100,13 +147,8 @@ static void oracle_row(const oracle_job *J, int64_t flat, double *o, double *lse
     const float *kbase = J->k + (b * J->Hkv + hk) * J->Lk * D;
     const float *vbase = J->v + (b * J->Hkv + hk) * J->Lk * D;
 
-    /* the visible keys form one interval [jlo, jhi) */
-    int64_t jlo = 0, jhi = J->Lk;
-    if (J->causal && p + 1 < jhi) jhi = p + 1;
-    if (J->window) {
-        if (J->window_left >= 0 && p - J->window_left > jlo) jlo = p - J->window_left;
-        if (J->window_right >= 0 && p + J->window_right + 1 < jhi) jhi = p + J->window_right + 1;
-    }
+    int64_t jlo, jhi;
+    visible_keys(J, p, &jlo, &jhi);
 
     for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
     if (jhi <= jlo) {
@@ -114,23 +156,7 @@ static void oracle_row(const oracle_job *J, int64_t flat, double *o, double *lse
         return;
     }
 
-    /* scores of the visible keys (s[j - jlo]) */
-    for (int64_t j = jlo; j < jhi; ++j) {
-        const float *krow = kbase + j * D;
-        double dot = 0.0;
-        for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (double)krow[d];
-        double sj = J->scale * dot;
-        if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);
-        if (J->bias_kind == ORACLE_BIAS_DENSE) {
-            const int64_t *st = J->bias_strides;
-            sj += (double)J->bias[b * st[0] + h * st[1] + i * st[2] + j * st[3]];
-        } else if (J->bias_kind == ORACLE_BIAS_ALIBI) {
-            double dist = (double)(p - j);
-            if (dist < 0) dist = -dist;
-            sj += -(double)J->slopes[h] * dist;
-        }
-        s[j - jlo] = sj;
-    }
+    row_scores(J, b, h, i, p, jlo, jhi, qrow, kbase, s, 0);
 
     /* pass 1: the row maximum */
     double m = -INFINITY;
@@ -299,4 +325,182 @@ int oracle_splitk_combine(int64_t rows, int64_t S, int64_t D,
         lse[r] = M + log(L);
     }
     return 0;
+}
+
+/*
+ * oracle_attention_bwd: gradients of the attention forward above, in fp64.
+ *
+ * For each row (b, h, i) with forward weights P_j = exp(s_j - LSE) over its
+ * visible keys (the definition of oracle_attention, recomputed here) and an
+ * output gradient dO_i, the chain rule through O_i = sum_j P_j v_j, the
+ * softmax, the soft cap and the scale gives
+ *   dv_j  += P_j dO_i
+ *   dP_j   = dO_i . v_j,   Delta_i = sum_j P_j dP_j  (= dO_i . O_i)
+ *   dS_j   = P_j (dP_j - Delta_i)                    (softmax Jacobian)
+ *   dU_j   = dS_j * (1 - tanh^2(u_j / c))  with a cap c, else dS_j
+ *            (u_j = scale * q_i . k_j; d/du [c tanh(u / c)] = 1 - tanh^2(u / c);
+ *             the bias is a constant and passes dS_j through unchanged)
+ *   dq_i  += scale * dU_j k_j,   dk_j += scale * dU_j q_i.
+ * K/V head hk collects the gradients of every query head of its group (the
+ * GQA sharing of [Mirage lecture] section 7.1).  No bias gradient is formed.
+ * A row with no visible key (or only -inf scores) contributes nothing and
+ * gets dq = 0.  The pages give the backward pass only by its shape ([Twill
+ * review] section 7.2: one pass with five matrix products and one
+ * exponential, benchmarked non-causal at batch 4, 32 heads, head dim 128);
+ * the gradient itself is the plain derivative of the forward definition.
+ *
+ * Work is split by (b, hk): each unit owns dk, dv of its K/V head and dq of
+ * the rows of its query heads, so no two threads write the same element.
+ */
+typedef struct {
+    oracle_job f;              /* forward problem (rows, o, lse unused) */
+    const float *dout;
+    double *dq, *dk, *dv;
+    int64_t next_unit;
+} oracle_bwd_job;
+
+static void oracle_bwd_unit(oracle_bwd_job *W, int64_t unit, double *s, double *dc, double *orow)
+{
+    const oracle_job *J = &W->f;
+    const int64_t b = unit / J->Hkv, hk = unit % J->Hkv;
+    const int64_t G = J->Hq / J->Hkv, D = J->D;
+    const float *kbase = J->k + (b * J->Hkv + hk) * J->Lk * D;
+    const float *vbase = J->v + (b * J->Hkv + hk) * J->Lk * D;
+    double *dkbase = W->dk + (b * J->Hkv + hk) * J->Lk * D;
+    double *dvbase = W->dv + (b * J->Hkv + hk) * J->Lk * D;
+
+    for (int64_t h = hk * G; h < (hk + 1) * G; ++h) {
+        for (int64_t i = 0; i < J->Lq; ++i) {
+            const int64_t p = (J->Lk - J->Lq) + i;   /* as in the forward */
+            const int64_t row = (b * J->Hq + h) * J->Lq + i;
+            const float *qrow = J->q + row * D;
+            const float *dorow = W->dout + row * D;
+            double *dqrow = W->dq + row * D;
+
+            int64_t jlo, jhi;
+            visible_keys(J, p, &jlo, &jhi);
+            if (jhi <= jlo) continue;
+
+            /* forward scores, and the cap's slope */
+            row_scores(J, b, h, i, p, jlo, jhi, qrow, kbase, s, dc);
+            double m = -INFINITY;
+            for (int64_t j = jlo; j < jhi; ++j)
+                if (s[j - jlo] > m) m = s[j - jlo];
+            if (m == -INFINITY) continue;
+            double l = 0.0;
+            for (int64_t j = jlo; j < jhi; ++j) l += exp(s[j - jlo] - m);
+
+            /* P, O, Delta */
+            for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+            for (int64_t j = jlo; j < jhi; ++j) {
+                s[j - jlo] = exp(s[j - jlo] - m) / l;          /* now P_j */
+                const float *vrow = vbase + j * D;
+                for (int64_t d = 0; d < D; ++d) orow[d] += s[j - jlo] * (double)vrow[d];
+            }
+            double delta = 0.0;
+            for (int64_t d = 0; d < D; ++d) delta += (double)dorow[d] * orow[d];
+
+            /* gradients */
+            for (int64_t j = jlo; j < jhi; ++j) {
+                const double P = s[j - jlo];
+                const float *vrow = vbase + j * D;
+                const float *krow = kbase + j * D;
+                double dP = 0.0;
+                for (int64_t d = 0; d < D; ++d) dP += (double)dorow[d] * (double)vrow[d];
+                const double dU = P * (dP - delta) * dc[j - jlo];
+                double *dkrow = dkbase + j * D, *dvrow = dvbase + j * D;
+                for (int64_t d = 0; d < D; ++d) {
+                    dqrow[d] += J->scale * dU * (double)krow[d];
+                    dkrow[d] += J->scale * dU * (double)qrow[d];
+                    dvrow[d] += P * (double)dorow[d];
+                }
+            }
+        }
+    }
+}
+
+static void *oracle_bwd_worker(void *arg)
+{
+    oracle_bwd_job *W = (oracle_bwd_job *)arg;
+    const int64_t n = W->f.Lk > 0 ? W->f.Lk : 1;
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double *dc = (double *)malloc(sizeof(double) * (size_t)n);
+    double *orow = (double *)malloc(sizeof(double) * (size_t)W->f.D);
+    if (!s || !dc || !orow) {
+        free(s); free(dc); free(orow);
+        return (void *)1;
+    }
+    const int64_t units = W->f.B * W->f.Hkv;
+    for (;;) {
+        pthread_mutex_lock(&W->f.lock);
+        const int64_t u = W->next_unit;
+        W->next_unit += 1;
+        pthread_mutex_unlock(&W->f.lock);
+        if (u >= units) break;
+        oracle_bwd_unit(W, u, s, dc, orow);
+    }
+    free(s); free(dc); free(orow);
+    return 0;
+}
+
+/*
+ * q [B,Hq,Lq,D], k and v [B,Hkv,Lk,D], dout [B,Hq,Lq,D]: contiguous fp32;
+ * the other arguments as for oracle_attention.  dq [B,Hq,Lq,D], dk and dv
+ * [B,Hkv,Lk,D] are written in fp64.  Returns 0, -1 (invalid argument) or -2.
+ */
+int oracle_attention_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                         const float *q, const float *k, const float *v, const float *dout,
+                         double scale, int causal, double softcap,
+                         int window, int64_t window_left, int64_t window_right,
+                         int bias_kind, const float *bias, const int64_t *bias_strides,
+                         const float *slopes,
+                         double *dq, double *dk, double *dv, int nthreads)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || Lq < 0 || Lk < 0 || D < 1) return -1;
+    if (Hq % Hkv != 0) return -1;
+    if ((B * Hq * Lq > 0 && (!q || !dout || !dq)) || (B * Hkv * Lk > 0 && (!k || !v || !dk || !dv))) return -1;
+    if (bias_kind < 0 || bias_kind > 2) return -1;
+    if (bias_kind == ORACLE_BIAS_DENSE && (!bias || !bias_strides)) return -1;
+    if (bias_kind == ORACLE_BIAS_ALIBI && !slopes) return -1;
+    if (!(softcap >= 0.0) || window < 0 || window > 1) return -1;
+
+    for (int64_t t = 0; t < B * Hq * Lq * D; ++t) dq[t] = 0.0;
+    for (int64_t t = 0; t < B * Hkv * Lk * D; ++t) { dk[t] = 0.0; dv[t] = 0.0; }
+
+    oracle_bwd_job W;
+    oracle_job *J = &W.f;
+    J->B = B; J->Hq = Hq; J->Hkv = Hkv; J->Lq = Lq; J->Lk = Lk; J->D = D;
+    J->q = q; J->k = k; J->v = v;
+    J->scale = scale; J->causal = causal;
+    J->softcap = softcap; J->window = window;
+    J->window_left = window_left; J->window_right = window_right;
+    J->bias_kind = bias_kind; J->bias = bias; J->slopes = slopes;
+    for (int t = 0; t < 4; ++t) J->bias_strides[t] = bias_strides ? bias_strides[t] : 0;
+    J->rows = 0; J->nrows = 0; J->o = 0; J->lse = 0; J->next_row = 0;
+    pthread_mutex_init(&J->lock, 0);
+    W.dout = dout; W.dq = dq; W.dk = dk; W.dv = dv; W.next_unit = 0;
+
+    const int64_t units = B * Hkv;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > units) nthreads = units > 0 ? (int)units : 1;
+    int rc = 0;
+    if (nthreads == 1) {
+        if (oracle_bwd_worker(&W)) rc = -2;
+    } else {
+        pthread_t th[256];
+        int started = 0;
+        for (int t = 0; t < nthreads; ++t) {
+            if (pthread_create(&th[t], 0, oracle_bwd_worker, &W) != 0) break;
+            ++started;
+        }
+        if (started == 0 && oracle_bwd_worker(&W)) rc = -2;
+        for (int t = 0; t < started; ++t) {
+            void *ret = 0;
+            pthread_join(th[t], &ret);
+            if (ret) rc = -2;
+        }
+    }
+    pthread_mutex_destroy(&J->lock);
+    return rc;
 }

@@ -20,8 +20,13 @@ The oracle is checked against things other than itself:
 * the split-K combine against the unsplit oracle over several chunkings, with
   arbitrary per-chunk reference values ("subtracting any m gives the same",
   Mirage lecture section 5.5) and empty chunks;
+* the backward (dQ, dK, dV) against central finite differences of the scipy
+  brute force, and invariants: value gradients add up to the output gradients,
+  key gradients add up to zero, equal keys give dQ = 0, Q = 0 gives dV in
+  closed form;
 * planted mistakes: copies of the oracle with a plausible error each (wrong kv
-  head, dropped scale, bias sign, causal off-by-one, log base, combine weight)
+  head, dropped scale, bias sign, causal off-by-one, log base, combine weight,
+  dropped Delta, missing cap slope, wrong head group in the backward, ...)
   are compiled and must fail these pins.
 """
 import json
@@ -620,22 +625,227 @@ def test_combine_exact_weights():
 
 
 # ----------------------------------------------------------------------------
+# backward: gradients of the forward definition
+# ----------------------------------------------------------------------------
+# The pages give the backward pass only by its shape (Twill review, section 7.2:
+# one pass, five matrix products, one exponential); its values are the
+# derivatives of the forward definition pinned above.  They are pinned here by
+# central finite differences of the scipy brute force, sum(dO * O), which shares
+# nothing with the oracle, and by invariants of the softmax.
+BWD_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, scale, causal, bias, softcap, window
+    (1, 2, 1, 5, 7, 4, 0.5, True, None, 0.0, None),            # causal, Lq < Lk, GQA
+    (1, 2, 2, 6, 6, 3, 0.7, False, "dense_inf", 0.0, None),    # dense bias with -inf entries and a dead row
+    (2, 4, 2, 4, 9, 4, 0.4, False, "alibi", 0.0, (2, 1)),      # window, ALiBi
+    (1, 3, 1, 5, 5, 4, 0.9, True, None, 1.5, None),            # strong soft cap, G = 3
+    (1, 2, 1, 6, 4, 4, 0.6, True, None, 0.0, None),            # Lq > Lk: rows without keys
+    (1, 2, 1, 5, 8, 4, 0.5, False, "dense", 2.0, (1, 0)),      # cap, window and dense bias
+]
+
+
+def _bwd_inputs(case, rng):
+    B, Hq, Hkv, Lq, Lk, D, scale, causal, bias_kind, softcap, window = case
+    q = rng.standard_normal((B, Hq, Lq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, Lk, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, Lk, D)).astype(np.float32)
+    do = rng.standard_normal((B, Hq, Lq, D)).astype(np.float32)
+    kw, bkw = {"softcap": softcap, "window": window}, {"softcap": softcap, "window": window}
+    if bias_kind in ("dense", "dense_inf"):
+        bias = rng.standard_normal((B, Hq, Lq, Lk)).astype(np.float32)
+        if bias_kind == "dense_inf":
+            bias[:, :, 0, :] = -np.inf          # a row with no usable key
+            bias[:, :, 1, 2] = -np.inf
+            bias[:, 1, 3, ::2] = -np.inf
+        kw["bias"] = bkw["bias"] = bias
+    elif bias_kind == "alibi":
+        slopes = np.power(2.0, -8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        kw["alibi_slopes"] = bkw["slopes"] = slopes
+    return q, k, v, do, scale, causal, kw, bkw
+
+
+def check_bwd_finite_differences(case, lib=None, elems=None, h=1e-5, tol=2e-7):
+    """Every (or ``elems`` spread) element of dQ, dK, dV against the central
+    difference of L = sum(dO * O) with O from the scipy brute force in fp64."""
+    rng = np.random.default_rng(31)
+    q, k, v, do, scale, causal, kw, bkw = _bwd_inputs(case, rng)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, causal, lib=lib, **kw)
+    base = [np.asarray(x, np.float64) for x in (q, k, v)]
+    dod = np.asarray(do, np.float64)
+
+    def loss(arrs):
+        O, _ = brute(arrs[0], arrs[1], arrs[2], scale, causal, **bkw)
+        return float(np.sum(dod * O))
+
+    for which, grad in enumerate((dq, dk, dv)):
+        n = grad.size
+        idx = range(n) if elems is None else np.linspace(0, n - 1, min(elems, n)).astype(int)
+        for t in idx:
+            plus = [a.copy() for a in base]
+            minus = [a.copy() for a in base]
+            plus[which].reshape(-1)[t] += h
+            minus[which].reshape(-1)[t] -= h
+            fd = (loss(plus) - loss(minus)) / (2 * h)
+            got = grad.reshape(-1)[t]
+            assert abs(got - fd) <= tol * max(1.0, abs(fd)), \
+                "%s[%d]: oracle %.9f, finite difference %.9f" % ("qkv"[which], t, got, fd)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[str(i) for i in range(len(BWD_CASES))])
+def test_bwd_finite_differences(case):
+    check_bwd_finite_differences(case)
+
+
+def _visible_rows(B, Hq, Lq, Lk, causal, window):
+    """[B, Hq, Lq] bool: the row sees at least one key."""
+    pos = np.arange(Lq) + (Lk - Lq)
+    lo = np.zeros(Lq, np.int64)
+    hi = np.full(Lq, Lk, np.int64)
+    if causal:
+        hi = np.minimum(hi, pos + 1)
+    if window is not None:
+        if window[0] >= 0:
+            lo = np.maximum(lo, pos - window[0])
+        if window[1] >= 0:
+            hi = np.minimum(hi, pos + window[1] + 1)
+    return np.broadcast_to(hi > lo, (B, Hq, Lq))
+
+
+@pytest.mark.parametrize("causal,window,alibi", [(False, None, False), (True, None, True),
+                                                 (True, (5, -1), False), (False, (3, 2), True)])
+def test_bwd_invariants(causal, window, alibi):
+    """Without a cap: the value gradients of a K/V head add up to the output
+    gradients of the rows that see a key (each softmax row sums to 1), and the
+    key gradients add up to zero (a shift of every key by the same vector adds
+    a constant to each score row, which the softmax ignores)."""
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 24, 40, 8
+    q, k, v, do = (rng.standard_normal(s).astype(np.float32)
+                   for s in ((B, Hq, Lq, D), (B, Hkv, Lk, D), (B, Hkv, Lk, D), (B, Hq, Lq, D)))
+    kw = {"window": window}
+    if alibi:
+        kw["alibi_slopes"] = np.power(2.0, -np.arange(1, Hq + 1)).astype(np.float32)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.4, causal, **kw)
+    vis = _visible_rows(B, Hq, Lq, Lk, causal, window)
+    G = Hq // Hkv
+    want = np.where(vis[..., None], do.astype(np.float64), 0.0).reshape(B, Hkv, G * Lq, D).sum(axis=2)
+    np.testing.assert_allclose(dv.sum(axis=2), want, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-10)
+    assert np.all(dq[~vis] == 0.0)
+
+
+def test_bwd_identical_keys_give_zero_dq():
+    """All keys equal: every score of a row is the same function of q, so the
+    weights do not depend on q (also under a cap, whose slope is then equal
+    for all keys) and dQ = 0."""
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((1, 2, 6, 8)).astype(np.float32)
+    k = np.repeat(rng.standard_normal((1, 1, 1, 8)).astype(np.float32), 10, axis=2)
+    v = rng.standard_normal((1, 1, 10, 8)).astype(np.float32)
+    do = rng.standard_normal((1, 2, 6, 8)).astype(np.float32)
+    for softcap in (0.0, 1.0):
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.5, True, softcap=softcap)
+        np.testing.assert_allclose(dq, 0.0, atol=1e-12)
+
+
+def test_bwd_zero_q_value_gradient_closed_form():
+    """Q = 0 and no bias: each row weighs its visible keys equally, so
+    dV_j = sum over the rows i that see j of dO_i / (number of keys row i sees)."""
+    rng = np.random.default_rng(47)
+    Lq, Lk, D = 7, 11, 4
+    q = np.zeros((1, 1, Lq, D), np.float32)
+    k = rng.standard_normal((1, 1, Lk, D)).astype(np.float32)
+    v = rng.standard_normal((1, 1, Lk, D)).astype(np.float32)
+    do = rng.standard_normal((1, 1, Lq, D)).astype(np.float32)
+    _, _, dv = oracle.attention_bwd(q, k, v, do, 1.0, True, window=(3, -1))
+    want = np.zeros((Lk, D))
+    for i in range(Lq):
+        p = i + Lk - Lq
+        keys = [j for j in range(Lk) if p - 3 <= j <= p]
+        for j in keys:
+            want[j] += do[0, 0, i].astype(np.float64) / len(keys)
+    np.testing.assert_allclose(dv[0, 0], want, rtol=0, atol=1e-12)
+
+
+def test_bwd_empty_shapes():
+    rng = np.random.default_rng(53)
+    q = rng.standard_normal((1, 2, 3, 4)).astype(np.float32)
+    do = rng.standard_normal((1, 2, 3, 4)).astype(np.float32)
+    k = np.zeros((1, 1, 0, 4), np.float32)
+    dq, dk, dv = oracle.attention_bwd(q, k, k, do, 1.0, False)
+    assert dq.shape == (1, 2, 3, 4) and np.all(dq == 0) and dk.shape == (1, 1, 0, 4)
+    q0 = np.zeros((1, 2, 0, 4), np.float32)
+    k1 = rng.standard_normal((1, 1, 5, 4)).astype(np.float32)
+    dq, dk, dv = oracle.attention_bwd(q0, k1, k1, q0, 1.0, True)
+    assert dq.shape == (1, 2, 0, 4) and np.all(dk == 0) and np.all(dv == 0)
+
+
+def test_bwd_thread_count_does_not_matter():
+    rng = np.random.default_rng(59)
+    q, k, v, do = (rng.standard_normal(s).astype(np.float32)
+                   for s in ((2, 4, 9, 8), (2, 2, 13, 8), (2, 2, 13, 8), (2, 4, 9, 8)))
+    a = oracle.attention_bwd(q, k, v, do, 0.3, True, softcap=2.0, threads=1)
+    b = oracle.attention_bwd(q, k, v, do, 0.3, True, softcap=2.0, threads=7)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# ----------------------------------------------------------------------------
 # planted mistakes must be caught
 # ----------------------------------------------------------------------------
+CAP_THEN_BIAS = """        if (J->softcap > 0.0) {
+            const double th = tanh(sj / J->softcap);
+            sj = J->softcap * th;
+            slope = 1.0 - th * th;
+        }
+        if (J->bias_kind == ORACLE_BIAS_DENSE) {
+            const int64_t *st = J->bias_strides;
+            sj += (double)J->bias[b * st[0] + h * st[1] + i * st[2] + j * st[3]];
+        } else if (J->bias_kind == ORACLE_BIAS_ALIBI) {
+            double dist = (double)(p - j);
+            if (dist < 0) dist = -dist;
+            sj += -(double)J->slopes[h] * dist;
+        }
+"""
+BIAS_THEN_CAP = """        if (J->bias_kind == ORACLE_BIAS_DENSE) {
+            const int64_t *st = J->bias_strides;
+            sj += (double)J->bias[b * st[0] + h * st[1] + i * st[2] + j * st[3]];
+        } else if (J->bias_kind == ORACLE_BIAS_ALIBI) {
+            double dist = (double)(p - j);
+            if (dist < 0) dist = -dist;
+            sj += -(double)J->slopes[h] * dist;
+        }
+        if (J->softcap > 0.0) {
+            const double th = tanh(sj / J->softcap);
+            sj = J->softcap * th;
+            slope = 1.0 - th * th;
+        }
+"""
+
 MUTANTS = {
     "kv_head_modulo": ("const int64_t hk = h / G;", "const int64_t hk = h % J->Hkv;"),
-    "dropped_scale": ("double sj = J->scale * dot;", "double sj = dot;"),
+    "dropped_scale": ("double sj = J->scale * dot, slope = 1.0;", "double sj = dot, slope = 1.0;"),
     "alibi_sign": ("sj += -(double)J->slopes[h] * dist;", "sj += (double)J->slopes[h] * dist;"),
     "causal_off_by_one": ("if (J->causal && p + 1 < jhi) jhi = p + 1;", "if (J->causal && p < jhi) jhi = p;"),
-    "softcap_undivided": ("sj = J->softcap * tanh(sj / J->softcap);", "sj = J->softcap * tanh(sj);"),
-    "softcap_ignored": ("        if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);\n", "\n"),
-    "softcap_after_bias": ("        if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);\n"
-                           "        if (J->bias_kind == ORACLE_BIAS_DENSE) {",
-                           "        if (J->bias_kind == ORACLE_BIAS_DENSE) {"
-                           " if (J->softcap > 0.0) sj = J->softcap * tanh(sj / J->softcap);"),
+    "softcap_undivided": ("const double th = tanh(sj / J->softcap);", "const double th = tanh(sj);"),
+    "softcap_ignored": ("            sj = J->softcap * th;\n", "\n"),
+    "softcap_after_bias": (CAP_THEN_BIAS, BIAS_THEN_CAP),
     "window_left_off_by_one": ("jlo = p - J->window_left;", "jlo = p - J->window_left + 1;"),
     "window_right_off_by_one": ("jhi = p + J->window_right + 1;", "jhi = p + J->window_right;"),
     "causal_top_left": ("const int64_t p = i + (J->Lk - J->Lq);", "const int64_t p = i;"),
+    # backward
+    "bwd_dropped_delta": ("const double dU = P * (dP - delta) * dc[j - jlo];",
+                          "const double dU = P * dP * dc[j - jlo];"),
+    "bwd_no_cap_slope": ("const double dU = P * (dP - delta) * dc[j - jlo];",
+                         "const double dU = P * (dP - delta);"),
+    "bwd_cap_slope_tanh": ("slope = 1.0 - th * th;", "slope = 1.0 - th;"),
+    "bwd_dq_unscaled": ("dqrow[d] += J->scale * dU * (double)krow[d];", "dqrow[d] += dU * (double)krow[d];"),
+    "bwd_dk_from_k": ("dkrow[d] += J->scale * dU * (double)qrow[d];",
+                      "dkrow[d] += J->scale * dU * (double)krow[d];"),
+    "bwd_dv_from_ds": ("dvrow[d] += P * (double)dorow[d];", "dvrow[d] += dU * (double)dorow[d];"),
+    "bwd_delta_from_do": ("delta += (double)dorow[d] * orow[d];", "delta += (double)dorow[d] * (double)dorow[d];"),
+    "bwd_heads_interleaved": ("for (int64_t h = hk * G; h < (hk + 1) * G; ++h) {",
+                              "for (int64_t h = hk; h < J->Hq; h += J->Hkv) {"),
+    "bwd_unnormalised_p": ("s[j - jlo] = exp(s[j - jlo] - m) / l;", "s[j - jlo] = exp(s[j - jlo] - m);"),
     "lse_log2": ("*lse = m + log(l);", "*lse = m + log2(l);"),
     "missing_normalise": ("for (int64_t d = 0; d < D; ++d) o[d] /= l;", ";"),
     "combine_weight_sign": ("const double w = exp(ms - M);", "const double w = exp(M - ms);"),
@@ -680,6 +890,8 @@ def _pin_suite(lib):
         Oc, lc = oracle.splitk_combine(op, mp, lp, lib=lib)
         assert_close(Oc, O, 1e-6, "combine O")
         assert_close(lc, lse, 1e-6, "combine LSE")
+        for case in BWD_CASES:
+            check_bwd_finite_differences(case, lib=lib, elems=12)
     except AssertionError:
         return False
     return True
