@@ -1,6 +1,6 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) fused attention forward library
- * (libattn_mi355x.so).
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention library
+ * (libattn_mi355x.so): forward (prefill, split-K decode) and backward.
  *
  * The operation is the attention chain of "Neptune论文浅读：把FlashAttention式融合
  * 放进编译器" (gentlecold.top), section 2: S = scale * Q K^T, then the score
@@ -185,6 +185,64 @@ attn_status attn_validate_decode(const attn_fwd_args *a, int32_t num_splits,
 
 /* attn_fwd_args_size -- sizeof(attn_fwd_args), so a binding can check its mirror of the struct. */
 size_t attn_fwd_args_size(void);
+
+/*
+ * Backward pass
+ * -------------
+ * The gradients of the forward above with respect to q, k and v, for an
+ * output gradient dO.  The pages give the backward only by its shape (the
+ * review "Optimal Software Pipelining and Warp Specialization for Tensor Core
+ * GPUs", section 7.2: one pass over the tiles with five matrix products and
+ * one exponential, recomputing the weights from the saved log-sum-exp instead
+ * of storing them); the values are the plain derivatives of the forward
+ * definition.  With P_ij = exp(s_ij - LSE_i) (the saved LSE, natural log),
+ *     Delta_i = <dO_i, O_i>
+ *     dv_j    = sum_i P_ij dO_i
+ *     dS_ij   = P_ij (<dO_i, v_j> - Delta_i)           (softmax Jacobian)
+ *     dU_ij   = dS_ij (1 - tanh^2(t_ij / c))  with a soft cap c, else dS_ij
+ *     dq_i    = scale * sum_j dU_ij k_j,   dk_j = scale * sum_i dU_ij q_i,
+ * sums over the visible pairs; a K/V head collects the gradients of every
+ * query head of its group.  The bias receives no gradient.  A row with no
+ * visible key (LSE = -inf) gets dq = 0 and adds nothing.
+ */
+typedef struct attn_bwd_args {
+    attn_fwd_args fwd;               /* the forward problem as it was run: shapes, q, k, v, scale,
+                                        causal, bias, softcap, window.  fwd.o (element type
+                                        fwd.o_dtype, strides fwd.o_strides) and fwd.lse are READ:
+                                        they must hold that forward's outputs; fwd.lse is required */
+    const void *dout;                /* dO [B, Hq, Lq, D], element type fwd.dtype */
+    int64_t dout_strides[3];         /* b, h, l strides of dout in elements */
+    int32_t grad_dtype;              /* ATTN_F32 or ATTN_BF16: element type of dq, dk and dv */
+    int32_t reserved;                /* must be 0 */
+    void *dq;                        /* device, dQ [B, Hq, Lq, D], written */
+    int64_t dq_strides[3];
+    void *dk;                        /* device, dK [B, Hkv, Lk, D], written */
+    int64_t dk_strides[3];
+    void *dv;                        /* device, dV [B, Hkv, Lk, D], written */
+    int64_t dv_strides[3];
+    float *workspace;                /* device, attn_bwd_workspace_bytes(B, Hq, Lq) bytes, 16-byte
+                                        aligned; its contents on entry do not matter */
+} attn_bwd_args;
+
+/*
+ * attn_bwd -- writes dq, dk and dv (every element, also those of keys no
+ * query sees, which get 0).  bf16 q, k, v and dout only (fp32 inputs return
+ * ATTN_ERR_UNSUPPORTED), D in {64, 128}, the alignment rules of the forward
+ * for dout, dq, dk and dv.  dq, dk, dv and the workspace must not overlap
+ * each other or any input.  Two kernels run on the stream: the first forms
+ * Delta per query row together with dq, the second dk and dv; neither uses
+ * atomics, so the result is deterministic.
+ */
+attn_status attn_bwd(const attn_bwd_args *a, void *stream);
+
+/* attn_bwd_workspace_bytes -- workspace size for attn_bwd (2 fp32 per query row). */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq);
+
+/* attn_validate_bwd -- the host-side check attn_bwd runs (pure host function). */
+attn_status attn_validate_bwd(const attn_bwd_args *a);
+
+/* attn_bwd_args_size -- sizeof(attn_bwd_args). */
+size_t attn_bwd_args_size(void);
 
 /* attn_status_str -- static English text for a status code. */
 const char *attn_status_str(attn_status s);

@@ -1,4 +1,4 @@
-"""Python binding of the MI355X fused attention forward library.
+"""Python binding of the MI355X fused attention library (forward and backward).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libattn_mi355x.so`` behind the C ABI of ``include/attn.h``.
@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
     attn_fwd_prefill(q, k, v, ...)             -> (o, lse)
     attn_fwd_decode_splitk(q, k, v, splits, ...) -> (o_part, m_part, l_part)
     attn_splitk_combine(o_part, m_part, l_part, ...) -> (o, lse)
+    attn_bwd(q, k, v, o, lse, dout, ...)       -> (dq, dk, dv)
 and the conveniences ``prefill`` (= attn_fwd_prefill) and ``decode`` (split-K
 local step followed by the combine on the same stream).
 """
@@ -24,7 +25,8 @@ import torch
 __all__ = [
     "AttnError", "load_library", "library_path", "attn_fwd_prefill", "attn_fwd_decode_splitk",
     "attn_splitk_combine", "attn_decode_choose_splits", "attn_decode_partial_bytes",
-    "attn_device_cu_count", "prefill", "decode", "chunk_length", "AttnFwdArgs",
+    "attn_device_cu_count", "prefill", "decode", "chunk_length", "AttnFwdArgs", "AttnBwdArgs", "attn_bwd",
+    "attn_bwd_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +55,19 @@ class AttnFwdArgs(ctypes.Structure):
         ("o", ctypes.c_void_p), ("o_strides", _I64x3), ("lse", ctypes.c_void_p),
         ("softcap", ctypes.c_float), ("window", ctypes.c_int32),
         ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+    ]
+
+
+class AttnBwdArgs(ctypes.Structure):
+    """Mirror of ``attn_bwd_args`` in include/attn.h."""
+    _fields_ = [
+        ("fwd", AttnFwdArgs),
+        ("dout", ctypes.c_void_p), ("dout_strides", _I64x3),
+        ("grad_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("dq", ctypes.c_void_p), ("dq_strides", _I64x3),
+        ("dk", ctypes.c_void_p), ("dk_strides", _I64x3),
+        ("dv", ctypes.c_void_p), ("dv_strides", _I64x3),
+        ("workspace", ctypes.c_void_p),
     ]
 
 
@@ -100,8 +115,19 @@ def load_library():
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_fwd_args_size.argtypes = []
     lib.attn_fwd_args_size.restype = ctypes.c_size_t
+    PB = ctypes.POINTER(AttnBwdArgs)
+    lib.attn_bwd.argtypes = [PB, vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_validate_bwd.argtypes = [PB]
+    lib.attn_validate_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_args_size.argtypes = []
+    lib.attn_bwd_args_size.restype = ctypes.c_size_t
     if lib.attn_fwd_args_size() != ctypes.sizeof(AttnFwdArgs):
         raise ImportError("attn_fwd_args layout mismatch between include/attn.h and the binding")
+    if lib.attn_bwd_args_size() != ctypes.sizeof(AttnBwdArgs):
+        raise ImportError("attn_bwd_args layout mismatch between include/attn.h and the binding")
     _LIB = lib
     return lib
 
@@ -313,3 +339,57 @@ def decode(q, k, v, num_splits: Optional[int] = None, scale: Optional[float] = N
                                                     window=window)
     return attn_splitk_combine(o_part, m_part, l_part, out=out, out_dtype=out_dtype or q.dtype,
                                return_lse=return_lse)
+
+
+def attn_bwd_workspace_bytes(B: int, Hq: int, Lq: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Lq))
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool = False, *, bias=None,
+             alibi_slopes=None, softcap: float = 0.0, window: Optional[Tuple[int, int]] = None,
+             grad_dtype: Optional[torch.dtype] = None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dQ [B,Hq,Lq,D], dK [B,Hkv,Lk,D], dV [B,Hkv,Lk,D]) of attention
+    for the output gradient ``dout``.  ``o`` and ``lse`` are the forward's
+    outputs for the same arguments; the other arguments are as for
+    ``attn_fwd_prefill``.  ``workspace`` may be a GPU byte tensor of at least
+    ``attn_bwd_workspace_bytes(B, Hq, Lq)`` bytes to reuse."""
+    lib = load_library()
+    B, Hq, Lq, D = q.shape
+    _, Hkv, Lk, _ = k.shape
+    dev = q.device
+    for name, t in (("o", o), ("dout", dout)):
+        _check_4d(name, t)
+        if tuple(t.shape) != (B, Hq, Lq, D):
+            raise ValueError("%s must be [B, Hq, Lq, D]" % name)
+    if dout.dtype != q.dtype:
+        raise TypeError("dout must have the dtype of q")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq * Lq or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous GPU fp32 tensor of B*Hq*Lq elements")
+    gdt = grad_dtype or q.dtype
+    if dq is None:
+        dq = torch.empty((B, Hq, Lq, D), dtype=gdt, device=dev)
+    if dk is None:
+        dk = torch.empty((B, Hkv, Lk, D), dtype=gdt, device=dev)
+    if dv is None:
+        dv = torch.empty((B, Hkv, Lk, D), dtype=gdt, device=dev)
+    for name, t, shape in (("dq", dq, (B, Hq, Lq, D)), ("dk", dk, (B, Hkv, Lk, D)), ("dv", dv, (B, Hkv, Lk, D))):
+        _check_4d(name, t)
+        if tuple(t.shape) != shape or t.dtype != gdt:
+            raise ValueError("%s must be %s of dtype %s" % (name, shape, gdt))
+    need = attn_bwd_workspace_bytes(B, Hq, Lq)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor of at least %d bytes" % need)
+    a = AttnBwdArgs()
+    a.fwd = _make_args(q, k, v, scale, causal, bias, alibi_slopes, o, lse, softcap, window)
+    a.dout, a.dout_strides = _ptr(dout), _strides3(dout)
+    a.grad_dtype = _dtype_code(gdt)
+    a.dq, a.dq_strides = _ptr(dq), _strides3(dq)
+    a.dk, a.dk_strides = _ptr(dk), _strides3(dk)
+    a.dv, a.dv_strides = _ptr(dv), _strides3(dv)
+    a.workspace = _ptr(workspace)
+    st = lib.attn_bwd(ctypes.byref(a), _stream(dev))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

@@ -104,6 +104,9 @@ FwdParams make_params(const attn_fwd_args *a) {
     return p;
 }
 
+// rows of one workspace array, rounded up to 16 bytes
+int64_t bwd_rows_padded(int64_t rows) { return (rows + 3) / 4 * 4; }
+
 int32_t chunk_len(int64_t Lk, int32_t S) {
     const int64_t per = (Lk + (int64_t)S * 32 - 1) / ((int64_t)S * 32);
     return (int32_t)(per < 1 ? 32 : per * 32);
@@ -230,6 +233,70 @@ int32_t attn_device_cu_count(int32_t device) {
 }
 
 size_t attn_fwd_args_size(void) { return sizeof(attn_fwd_args); }
+
+size_t attn_bwd_args_size(void) { return sizeof(attn_bwd_args); }
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq) {
+    if (B < 0 || Hq < 0 || Lq < 0) return 0;
+    return 2 * bwd_rows_padded(B * Hq * Lq) * sizeof(float);
+}
+
+attn_status attn_validate_bwd(const attn_bwd_args *a) {
+    if (a == nullptr) return ATTN_ERR_INVALID_ARG;
+    const attn_fwd_args *f = &a->fwd;
+    attn_status st = check_common(f);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(f->o_dtype) || !valid_dtype(a->grad_dtype) || a->reserved != 0) return ATTN_ERR_INVALID_ARG;
+    for (int t = 0; t < 3; ++t)
+        if (f->o_strides[t] < 0 || a->dout_strides[t] < 0 || a->dq_strides[t] < 0 || a->dk_strides[t] < 0 ||
+            a->dv_strides[t] < 0)
+            return ATTN_ERR_INVALID_ARG;
+    const bool any_q = f->B * f->Hq * f->Lq > 0;
+    const bool any_kv = f->B * f->Hkv * f->Lk > 0;
+    if (any_q && (f->o == nullptr || f->lse == nullptr || a->dout == nullptr || a->dq == nullptr ||
+                  a->workspace == nullptr))
+        return ATTN_ERR_INVALID_ARG;
+    if (any_kv && (a->dk == nullptr || a->dv == nullptr)) return ATTN_ERR_INVALID_ARG;
+    if (f->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    // one-dimensional grids of 128-row (query or key) tiles
+    if (f->B * f->Hq * ((f->Lq + 127) / 128) > kIntMax || f->B * f->Hkv * ((f->Lk + 127) / 128) > kIntMax)
+        return ATTN_ERR_UNSUPPORTED;
+    // 16-byte rows of o, dout and the gradients; 4-byte lse; 16-byte workspace
+    const int64_t ov = 16 / elem_size(f->o_dtype), gv = 16 / elem_size(a->grad_dtype), dv = 16 / elem_size(f->dtype);
+    if (any_q) {
+        if (!aligned(f->o, 16) || !aligned(a->dout, 16) || !aligned(a->dq, 16)) return ATTN_ERR_UNSUPPORTED;
+        if (!aligned(f->lse, 4) || !aligned(a->workspace, 16)) return ATTN_ERR_INVALID_ARG;
+        for (int t = 0; t < 3; ++t)
+            if (f->o_strides[t] % ov || a->dout_strides[t] % dv || a->dq_strides[t] % gv) return ATTN_ERR_UNSUPPORTED;
+        if (a->dout_strides[2] > (1 << 24) || f->q_strides[2] > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+    }
+    if (any_kv) {
+        if (!aligned(a->dk, 16) || !aligned(a->dv, 16)) return ATTN_ERR_UNSUPPORTED;
+        for (int t = 0; t < 3; ++t)
+            if (a->dk_strides[t] % gv || a->dv_strides[t] % gv) return ATTN_ERR_UNSUPPORTED;
+    }
+    return ATTN_OK;
+}
+
+attn_status attn_bwd(const attn_bwd_args *a, void *stream) {
+    attn_status st = attn_validate_bwd(a);
+    if (st != ATTN_OK) return st;
+    const attn_fwd_args *f = &a->fwd;
+    if (f->B * f->Hq * f->Lq == 0 && f->B * f->Hkv * f->Lk == 0) return ATTN_OK;
+    attn::BwdParams p{};
+    p.f = make_params(f);
+    p.dout = a->dout;
+    p.do_sb = a->dout_strides[0]; p.do_sh = a->dout_strides[1]; p.do_sl = a->dout_strides[2];
+    p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+    p.dq_sb = a->dq_strides[0]; p.dq_sh = a->dq_strides[1]; p.dq_sl = a->dq_strides[2];
+    p.dk_sb = a->dk_strides[0]; p.dk_sh = a->dk_strides[1]; p.dk_sl = a->dk_strides[2];
+    p.dv_sb = a->dv_strides[0]; p.dv_sh = a->dv_strides[1]; p.dv_sl = a->dv_strides[2];
+    p.delta = a->workspace;
+    p.lse_l2 = a->workspace + bwd_rows_padded(f->B * f->Hq * f->Lq);
+    p.grad_bf16 = a->grad_dtype == ATTN_BF16;
+    hipError_t err = attn::launch_bwd_bf16(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
 
 const char *attn_status_str(attn_status s) {
     switch (s) {

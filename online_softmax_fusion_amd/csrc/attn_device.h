@@ -74,6 +74,24 @@ __device__ __forceinline__ void store16(void *p, const u32x4 &v) {
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// Buffer descriptor over `bytes` bytes from `base`: loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 4 bf16 values from LDS through the transposing read: within each group of
+// 16 lanes, lane i receives element (i % 4) of the 8-byte words addressed by
+// lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// s_waitcnt with vmcnt = 0 and the other counters left alone (gfx9 encoding)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Swap bits 2 and 3 of a row index inside a 32-row block.  Loading key
 // perm32(r) into matrix-core row r makes the accumulator of S^T = K Q^T hold,
 // in lane l, keys 8*(l/32) + 0..7 in elements 0..7 and 16 + 8*(l/32) + 0..7 in

@@ -61,6 +61,43 @@ __host__ __device__ inline void key_range(const FwdParams &p, int pos, int &jmin
     jmax = (int)hi;
 }
 
+// Query rows [imin, imax] that see key j (0 <= j < Lk), the inverse of
+// key_range: row i sees j iff jmin(i + Lk - Lq) <= j <= jmax(i + Lk - Lq).
+// Both ends are non-decreasing in j.  imax < imin means no row sees j.
+__host__ __device__ inline void query_range(const FwdParams &p, int j, int &imin, int &imax) {
+    const int64_t off = (int64_t)p.Lk - p.Lq;
+    int64_t plo = -((int64_t)1 << 40), phi = (int64_t)1 << 40;   // positions i + off that see j
+    if (p.causal && (int64_t)j > plo) plo = j;
+    if (p.window) {
+        if (p.win_right >= 0 && (int64_t)j - p.win_right > plo) plo = (int64_t)j - p.win_right;
+        if (p.win_left >= 0 && (int64_t)j + p.win_left < phi) phi = (int64_t)j + p.win_left;
+    }
+    int64_t lo = plo - off, hi = phi - off;
+    if (lo < 0) lo = 0;
+    if (hi > (int64_t)p.Lq - 1) hi = (int64_t)p.Lq - 1;
+    if (j < 0 || j >= p.Lk || hi < lo) {
+        lo = 0;
+        hi = -1;
+    }
+    imin = (int)lo;
+    imax = (int)hi;
+}
+
+// Gradients of one attention problem (the forward problem plus dO and the
+// outputs).  Strides are in elements.
+struct BwdParams {
+    FwdParams f;                        // f.o: the forward's output (read); f.lse: its LSE (read)
+    const void *dout;
+    int64_t do_sb, do_sh, do_sl;
+    void *dq, *dk, *dv;
+    int64_t dq_sb, dq_sh, dq_sl;
+    int64_t dk_sb, dk_sh, dk_sl;
+    int64_t dv_sb, dv_sh, dv_sl;
+    float *delta;                       // [B*Hq*Lq] <dO_i, O_i>, written by the dQ kernel
+    float *lse_l2;                      // [B*Hq*Lq] LSE in log2 units (+inf for an empty row), same
+    int grad_bf16;                      // 1: dq, dk, dv are bf16, 0: fp32
+};
+
 struct CombineParams {
     const float *o_part, *m_part, *l_part;
     void *o;
@@ -78,5 +115,7 @@ hipError_t launch_decode_bf16(const FwdParams &p, hipStream_t stream);
 hipError_t launch_rows_f32(const FwdParams &p, int partial, hipStream_t stream);
 // log-sum-exp combine of split-K partials.
 hipError_t launch_combine(const CombineParams &c, hipStream_t stream);
+// bf16 backward: dQ (and Delta, LSE in log2 units), then dK and dV.
+hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t stream);
 
 }  // namespace attn

@@ -51,20 +51,6 @@ namespace {
 constexpr float kTau = 8.0f;
 constexpr int kXcds = 8;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// 4 bf16 values from LDS through the transposing read: within each group of
-// 16 lanes, lane i receives element (i % 4) of the 8-byte words addressed by
-// lanes 4j + i/4, j = 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
-
 template <int D>
 struct TileCfg {
     static constexpr int BC = 64;          // keys per tile
@@ -251,9 +237,6 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, co
                 (int)vgoff, (int)(i_ * RROWS * vl_bytes), 0, 0);                                                                            \
         }                                                                                                       \
     } while (0)
-
-// s_waitcnt with vmcnt = 0 and the other counters left alone (gfx9 encoding)
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, int NW, int BIAS, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {

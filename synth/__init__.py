@@ -6,7 +6,8 @@ imports the other; both take their inputs from here.
 
 Recipe (one stream per tensor):
   * Q, K, V ~ N(0, 1), drawn in fp32 by ``torch.randn`` from a ``torch.Generator``
-    seeded with ``seed * 16 + tensor_id`` (Q = 0, K = 1, V = 2, dense bias = 3),
+    seeded with ``seed * 16 + tensor_id`` (Q = 0, K = 1, V = 2, dense bias = 3,
+    output gradient dO = 4),
     then rounded to bf16 (round-to-nearest-even, torch's cast) when the
     workload's dtype is bf16.  The oracle receives the stored values widened
     exactly to fp32/fp64.
@@ -28,7 +29,7 @@ from typing import Optional
 
 import torch
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_BIAS = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_BIAS, TENSOR_DOUT = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -81,8 +82,14 @@ SOFTCAP_PREFILL = Workload("softcap50-causal-prefill-bf16-B4-H32-L4096-d128", 4,
 WINDOW_PREFILL = Workload("window4096-causal-prefill-bf16-B1-H8-L32768-d128", 1, 8, 8, 32768, 32768, 128,
                           "bf16", True, "none", 1007, window=(4095, -1))
 
+# The backward pass on the shape the Twill review benchmarks it on (section
+# 7.2: non-causal, batch 4, 32 heads, head dim 128; its sequence lengths run up
+# to 16384), at 4096 rows, with dO ~ N(0, 1).
+BWD_PREFILL = Workload("bwd-noncausal-bf16-B4-H32-L4096-d128", 4, 32, 32, 4096, 4096, 128,
+                       "bf16", False, "none", 1008)
+
 WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PREFILL, C5_DECODE,
-                                 SOFTCAP_PREFILL, WINDOW_PREFILL)}
+                                 SOFTCAP_PREFILL, WINDOW_PREFILL, BWD_PREFILL)}
 
 
 def torch_dtype(name: str) -> torch.dtype:
@@ -120,3 +127,8 @@ def make_dense_bias(w: Workload, shape=None, dtype: str = "f32", device="cpu") -
     """A random additive bias, N(0,1), default shape [Hq, Lq, Lk] (broadcast over B)."""
     shape = shape if shape is not None else (w.Hq, w.Lq, w.Lk)
     return normal(shape, w.seed, TENSOR_BIAS, dtype, device)
+
+
+def make_dout(w: Workload, device="cpu") -> torch.Tensor:
+    """Output gradient dO [B,Hq,Lq,D], N(0,1), in the workload's dtype."""
+    return normal((w.B, w.Hq, w.Lq, w.D), w.seed, TENSOR_DOUT, w.dtype, device)

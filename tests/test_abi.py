@@ -29,9 +29,9 @@ def lib():
     return attn.load_library()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd_prefill", "attn_fwd_decode_splitk", "attn_splitk_combine"):
+    for n in ("attn_fwd_prefill", "attn_fwd_decode_splitk", "attn_splitk_combine", "attn_bwd"):
         assert n in names
 
 
@@ -42,6 +42,7 @@ def test_library_exports_every_declared_function(lib):
 
 def test_struct_layout_matches(lib):
     assert lib.attn_fwd_args_size() == ctypes.sizeof(attn.AttnFwdArgs) == 272
+    assert lib.attn_bwd_args_size() == ctypes.sizeof(attn.AttnBwdArgs) == 416
 
 
 def test_status_strings(lib):
@@ -162,3 +163,69 @@ def test_chunk_length():
     assert attn.chunk_length(1000, 3) == 352
     assert attn.chunk_length(100, 10) == 32
     assert attn.chunk_length(0, 4) == 32
+
+
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+P7, P8, P9, P10 = (0x10000 * (i + 7) for i in range(4))
+
+
+def good_bwd_args(grad_dtype=attn.ATTN_F32, D=128):
+    b = attn.AttnBwdArgs()
+    b.fwd = good_args(attn.ATTN_BF16, D)
+    b.dout = P6
+    b.dout_strides = (ctypes.c_int64 * 3)(8 * 64 * D, 64 * D, D)
+    b.grad_dtype = grad_dtype
+    b.dq, b.dk, b.dv = P7, P8, P9
+    b.dq_strides = (ctypes.c_int64 * 3)(8 * 64 * D, 64 * D, D)
+    b.dk_strides = (ctypes.c_int64 * 3)(2 * 96 * D, 96 * D, D)
+    b.dv_strides = (ctypes.c_int64 * 3)(2 * 96 * D, 96 * D, D)
+    b.workspace = P10
+    return b
+
+
+def test_bwd_valid_args_pass(lib):
+    assert lib.attn_validate_bwd(ctypes.byref(good_bwd_args())) == OK
+    assert lib.attn_validate_bwd(ctypes.byref(good_bwd_args(attn.ATTN_BF16, 64))) == OK
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda b: setattr(b.fwd, "lse", None), INVALID),        # the saved LSE is required
+    (lambda b: setattr(b.fwd, "o", None), INVALID),
+    (lambda b: setattr(b, "dout", None), INVALID),
+    (lambda b: setattr(b, "dq", None), INVALID),
+    (lambda b: setattr(b, "dk", None), INVALID),
+    (lambda b: setattr(b, "dv", None), INVALID),
+    (lambda b: setattr(b, "workspace", None), INVALID),
+    (lambda b: setattr(b, "workspace", P10 + 4), INVALID),
+    (lambda b: setattr(b, "grad_dtype", 5), INVALID),
+    (lambda b: setattr(b, "reserved", 1), INVALID),
+    (lambda b: b.dq_strides.__setitem__(1, -1), INVALID),
+    (lambda b: setattr(b.fwd, "causal", 3), INVALID),
+    (lambda b: setattr(b.fwd, "softcap", -2.0), INVALID),
+    (lambda b: setattr(b.fwd, "dtype", attn.ATTN_F32), UNSUPPORTED),   # fp32 inputs: forward only
+    (lambda b: setattr(b.fwd, "D", 96), UNSUPPORTED),
+    (lambda b: setattr(b, "dout", P6 + 2), UNSUPPORTED),
+    (lambda b: setattr(b, "dk", P8 + 8), UNSUPPORTED),
+    (lambda b: b.dv_strides.__setitem__(2, 130), UNSUPPORTED),
+])
+def test_bwd_rejects(lib, mutate, expect):
+    b = good_bwd_args()
+    mutate(b)
+    assert lib.attn_validate_bwd(ctypes.byref(b)) == expect
+    assert lib.attn_bwd(ctypes.byref(b), None) == expect
+
+
+def test_bwd_null_and_empty(lib):
+    assert lib.attn_bwd(None, None) == INVALID
+    b = good_bwd_args()
+    b.fwd.B = 0
+    assert lib.attn_bwd(ctypes.byref(b), None) == OK
+
+
+def test_bwd_workspace_bytes(lib):
+    # two fp32 arrays of B*Hq*Lq values, each rounded up to 16 bytes
+    assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 2 * 32 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 1, 4) == 32
+    assert lib.attn_bwd_workspace_bytes(0, 8, 8) == 0
