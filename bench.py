@@ -11,6 +11,11 @@ Default run (N = 1):
   * roofline -- for the dominant kernel of each leg, algorithmic work per
     launch / the average launch duration measured with HIP events on the
     stream the kernel runs on.
+  * backward leg -- attn_bwd (dQ kernel, then dK/dV kernel) on the shape the
+    Twill review benchmarks the backward on (non-causal, B=4, H=32, d=128),
+    at L=4096, with the forward's O and LSE as inputs.  Reported under
+    "backward" in algorithmic TFLOP/s: 10 * d FLOP per visible pair (the five
+    products S, dP, dV, dK, dQ), recomputation not counted.
   * cpu_baseline -- the fp64 oracle, timed on the host cores on a bounded
     sample of the prefill workload (whole heads), scaled to TFLOP/s.
 
@@ -80,6 +85,11 @@ def visible_pairs(Lq: int, Lk: int, causal: bool, window=None) -> int:
 def attention_flops(B, Hq, Lq, Lk, D, causal, window=None) -> int:
     """2*D FLOP for q.k and 2*D for p*v per visible pair."""
     return 4 * D * B * Hq * visible_pairs(Lq, Lk, causal, window)
+
+
+def backward_flops(B, Hq, Lq, Lk, D, causal, window=None) -> int:
+    """2*D FLOP for each of the five products (S, dP, dV, dK, dQ) per visible pair."""
+    return 10 * D * B * Hq * visible_pairs(Lq, Lk, causal, window)
 
 
 def prefill_bytes(B, Hq, Hkv, Lq, Lk, D, elem=2, o_elem=2) -> int:
@@ -228,6 +238,50 @@ def time_decode(w, steps, warmup, warm_s=1.0):
     return wall, avg_ms * 1e-3, S
 
 
+def time_backward(w, steps, warmup, warm_s=1.0):
+    """One step = one attn_bwd call (both kernels) on resident inputs; the
+    forward's O and LSE are computed once beforehand."""
+    import torch
+    import synth
+    import online_softmax_fusion_amd as attn
+
+    log("backward leg: %s, generating inputs" % w.name)
+    q, k, v = synth.make_qkv(w, device="cuda")
+    do = synth.make_dout(w, device="cuda")
+    kw = {"softcap": w.softcap, "window": w.window}
+    if w.bias == "alibi":
+        kw["alibi_slopes"] = synth.alibi_slopes(w.Hq).cuda()
+    scale = w.softmax_scale()
+    o, lse = attn.attn_fwd_prefill(q, k, v, scale, w.causal, **kw)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((attn.attn_bwd_workspace_bytes(w.B, w.Hq, w.Lq),), dtype=torch.uint8, device="cuda")
+
+    def step(i, evs=None):
+        if evs:
+            evs[0].record(torch.cuda.current_stream())
+        attn.attn_bwd(q, k, v, o, lse, do, scale, w.causal, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        if evs:
+            evs[1].record(torch.cuda.current_stream())
+
+    n = warm_up(step, warmup, warm_s)
+    log("backward: %d untimed warm-up steps" % n)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    durs = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_ms = sum(durs) / len(durs)
+    flops = backward_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal, w.window)
+    log("backward: step %.4f ms, kernels avg %.4f ms (p10 %.4f, p90 %.4f)" %
+        (wall * 1e3, avg_ms, durs[len(durs) // 10], durs[(9 * len(durs)) // 10]))
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return wall, avg_ms * 1e-3, flops
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle as it stands, on whole heads of the prefill workload."""
     import numpy as np
@@ -327,6 +381,8 @@ def main():
     ap.add_argument("--prefill", default=None, help="prefill workload name (default: causal B4 H32 L4096)")
     ap.add_argument("--decode", default=None, help="decode workload name (default: GQA B16 Lk32768)")
     ap.add_argument("--splits", type=int, default=None, help="override the decode split count")
+    ap.add_argument("--backward", default=None,
+                    help="backward workload name (default: non-causal B4 H32 L4096), or 'none' to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -371,6 +427,9 @@ def main():
     torch.cuda.synchronize()
     step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup, args.warm_seconds)
     d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup, args.warm_seconds)
+    wb = None if args.backward == "none" else synth.WORKLOADS[args.backward or synth.BWD_PREFILL.name]
+    if wb is not None:
+        b_step_s, b_kern_s, b_flops = time_backward(wb, args.steps, args.warmup, args.warm_seconds)
 
     p_tflops = flops / step_s / 1e12
     p_kern_tflops = flops / kern_s / 1e12
@@ -405,6 +464,14 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_kern_gbs / HBM_PEAK_GBS, 4),
                                 "traffic": measured_traffic("decode_bf16_kernel", wd.name, DECODE_SOURCES)}},
     }
+    if wb is not None:
+        b_kern_tflops = b_flops / b_kern_s / 1e12
+        result["backward"] = {
+            "workload": wb.name, "causal": wb.causal, "value": round(b_flops / b_step_s / 1e12, 2),
+            "unit": "TFLOP/s", "ms_per_step": round(b_step_s * 1e3, 4),
+            "roofline": {"kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
+                         "achieved": round(b_kern_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(b_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wp, args.cpu_budget)
     else:

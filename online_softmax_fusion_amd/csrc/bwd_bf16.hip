@@ -33,9 +33,10 @@
 // Both kernels read each streamed tile twice: as rows (16-byte reads along d)
 // and transposed (ds_read_b64_tr_b16 along the rows).  One XOR swizzle of the
 // 16-byte chunks serves both patterns without bank conflicts (see BwdCfg), so
-// each tile is stored once.  Tiles are double-buffered with direct
-// global->LDS loads, one barrier per tile; tiles that cross the causal
-// diagonal, the window edges or the end of the rows take a masked code path.
+// each tile is stored once.  Tiles are double-buffered in two LDS stages,
+// filled by buffer-to-LDS loads issued one tile ahead, one barrier per tile;
+// tiles that cross the causal diagonal, the window edges or the end of the
+// rows take a masked code path.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -142,19 +143,66 @@ __device__ __forceinline__ void store4(void *base, int64_t idx, bool bf16, float
     }
 }
 
-// Direct global->LDS load of a 64-row tile (rows [r0, r0 + 64) of rows
-// `base_`, `lbytes_` bytes apart, `nvalid_` of them present) into the LDS
-// tile `LDS_`: lane fills LDS bytes [i*T*16 + wave*1024 + 16*lane, +16) from
-// byte offset goff_ (+ round i's rows).  Missing rows read as zero.
-#define BWD_LOAD_TILE(LDS_, SRC_, LBYTES_, NVALID_, GOFF_)                                                      \
-    do {                                                                                                        \
-        const __amdgpu_buffer_rsrc_t rs_ = make_rsrc((SRC_), (uint32_t)((NVALID_) - 1) * (LBYTES_) + D * 2);    \
-        _Pragma("unroll") for (int i_ = 0; i_ < NC; ++i_) {                                                     \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
-                rs_, (__attribute__((address_space(3))) void *)((LDS_) + i_ * T * 16 + wave * 1024), 16,        \
-                (int)(GOFF_), (int)(i_ * RROWS * (LBYTES_)), 0, 0);                                             \
-        }                                                                                                       \
-    } while (0)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words: base address, stride 0, `bytes` readable bytes
+// (loads past the end read 0).
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// Buffer-to-LDS loads: 16 (or 4) bytes per lane from buffer offset voff + soff
+// into LDS at m0 + 16 * lane (4 * lane).  Inline assembly, so that the
+// compiler's wait insertion does not see them: the kernels wait for them
+// themselves (wait_all_loads) before the barrier that ends each tile.  Given
+// the LDS-DMA loads, the compiler drains every load in flight before LDS reads
+// it cannot prove independent, which serialises loading and computing.  No
+// compiler-generated instruction of this file may use M0.
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc),
+                 "s"(soff)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const i32x4 &rsrc, uint32_t m0, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+// every vector memory load of this wave has landed (also a compiler barrier)
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
+}
+
+// A 64-row tile (rows `src` .. + 63, `lbytes` apart, `nvalid` of them present)
+// into the LDS tile at byte address `lds`: lane fills LDS bytes
+// [i*T*16 + wave*1024 + 16*lane, +16) of round i from byte offset goff of the
+// source (+ round i's rows, RROWS rows per round).  Missing rows read as 0.
+template <int D, int T>
+__device__ __forceinline__ void dma_tile(const void *src, uint32_t lbytes, int nvalid, uint32_t lds, int wave,
+                                         uint32_t goff) {
+    using C = BwdCfg<D>;
+    constexpr int NC = C::TILE / (T * 16);
+    constexpr int RROWS = T * 16 / C::RB;
+    static_assert(NC >= 1 && C::TILE == NC * T * 16, "tile does not split evenly");
+    static_assert(RROWS % 16 == 0, "rounds must keep the swizzle");
+    const i32x4 rs = rsrc_words(src, (uint32_t)(nvalid - 1) * lbytes + D * 2);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) dma16(rs, lds + i * T * 16 + wave * 1024, goff, (uint32_t)(i * RROWS) * lbytes);
+}
+
+// this lane's source offset inside a tile: LDS position wave*1024 + 16*lane
+// holds chunk pc of row `row`, i.e. logical chunk pc ^ swz(row) of that row
+template <int D>
+__device__ __forceinline__ uint32_t tile_goff(int wave, int lane, uint32_t lbytes) {
+    using C = BwdCfg<D>;
+    const int pos = wave * 1024 + lane * 16;
+    const int row = pos / C::RB;
+    const int pc = (pos % C::RB) / 16;
+    return (uint32_t)row * lbytes + (uint32_t)((pc ^ C::swz(row)) * 16);
+}
 
 // ---------------------------------------------------------------------------
 // dQ kernel
@@ -219,15 +267,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     constexpr int BR = 32 * NW;
     constexpr int BC = C::BT;
     constexpr int T = NW * 64;
-    constexpr int NC = C::TILE / (T * 16);
-    constexpr int RROWS = T * 16 / C::RB;
-    static_assert(NC >= 1 && C::TILE == NC * T * 16, "tile does not split evenly");
-    static_assert(RROWS % 16 == 0, "rounds must keep the swizzle");
+    constexpr int STAGE = 2 * C::TILE;   // K tile, then V tile
 
-    __shared__ __attribute__((aligned(1024))) char lds_k0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char lds_k1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char lds_v0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char lds_v1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
     // work item: XCD-contiguous ranges of a head-major list, heavy tiles first
     const int nqt = (p.Lq + BR - 1) / BR;
@@ -327,14 +369,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     const int tbase = C::tr_base(lane);
     const uint32_t kl_bytes = (uint32_t)p.k_sl * 2u;
     const uint32_t vl_bytes = (uint32_t)p.v_sl * 2u;
-    uint32_t kgoff, vgoff;
-    {
-        const int pos = wave * 1024 + lane * 16;
-        const int row = pos / C::RB;
-        const int pc = (pos % C::RB) / 16;
-        kgoff = (uint32_t)row * kl_bytes + (uint32_t)((pc ^ C::swz(row)) * 16);
-        vgoff = (uint32_t)row * vl_bytes + (uint32_t)((pc ^ C::swz(row)) * 16);
-    }
+    const uint32_t kgoff = tile_goff<D>(wave, lane, kl_bytes);
+    const uint32_t vgoff = tile_goff<D>(wave, lane, vl_bytes);
+    const uint32_t lds0 = lds_addr(smem);
 
     f32x16 dqacc[C::DB];
 #pragma unroll
@@ -342,43 +379,32 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) dqacc[db][e] = 0.f;
 
-#define BWD_DQ_LOADS(TT_, KL_, VL_)                                                                             \
-    do {                                                                                                        \
-        const int j0_ = (TT_) * BC;                                                                             \
-        const int nv_ = min(BC, p.Lk - j0_);                                                                    \
-        BWD_LOAD_TILE(KL_, kp + (int64_t)j0_ * p.k_sl, kl_bytes, nv_, kgoff);                                   \
-        BWD_LOAD_TILE(VL_, vp + (int64_t)j0_ * p.v_sl, vl_bytes, nv_, vgoff);                                   \
-    } while (0)
-#define BWD_DQ_STEP(MASK_, BUF_, TT_)                                                                           \
-    dq_tile<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, rbase, tbase, qreg, doreg,    \
-                            dqacc, lse, delta, (TT_) * BC, wrow0, wjmin, wjmax, qpos, jmin, jmax, qrow, slope_l2, \
-                            b, h, lane)
-
+    // K/V tile t into stage `st`
+    auto issue = [&](int t, int st) {
+        const int j0 = t * BC;
+        const int nv = min(BC, p.Lk - j0);
+        const uint32_t dst = lds0 + st * STAGE;
+        dma_tile<D, T>(kp + (int64_t)j0 * p.k_sl, kl_bytes, nv, dst, wave, kgoff);
+        dma_tile<D, T>(vp + (int64_t)j0 * p.v_sl, vl_bytes, nv, dst + C::TILE, wave, vgoff);
+    };
     if (t_end > t_first) {
-        BWD_DQ_LOADS(t_first, lds_k0, lds_v0);
-        wait_vmem();
+        issue(t_first, 0);
+        wait_all_loads();
         __syncthreads();
     }
     for (int t = t_first; t < t_end; ++t) {
-        const bool masked = t < u_first || t >= u_end;
-        if (((t - t_first) & 1) == 0) {
-            if (t + 1 < t_end) BWD_DQ_LOADS(t + 1, lds_k1, lds_v1);
-            if (masked)
-                BWD_DQ_STEP(true, 0, t);
-            else
-                BWD_DQ_STEP(false, 0, t);
-        } else {
-            if (t + 1 < t_end) BWD_DQ_LOADS(t + 1, lds_k0, lds_v0);
-            if (masked)
-                BWD_DQ_STEP(true, 1, t);
-            else
-                BWD_DQ_STEP(false, 1, t);
-        }
-        wait_vmem();
+        const int st = (t - t_first) & 1;
+        if (t + 1 < t_end) issue(t + 1, st ^ 1);
+        const char *lk = smem + st * STAGE;
+        if (t < u_first || t >= u_end)
+            dq_tile<D, BIAS, true>(p, lk, lk + C::TILE, rbase, tbase, qreg, doreg, dqacc, lse, delta, t * BC, wrow0,
+                                   wjmin, wjmax, qpos, jmin, jmax, qrow, slope_l2, b, h, lane);
+        else
+            dq_tile<D, BIAS, false>(p, lk, lk + C::TILE, rbase, tbase, qreg, doreg, dqacc, lse, delta, t * BC, wrow0,
+                                    wjmin, wjmax, qpos, jmin, jmax, qrow, slope_l2, b, h, lane);
+        wait_all_loads();
         __syncthreads();
     }
-#undef BWD_DQ_STEP
-#undef BWD_DQ_LOADS
 
     if (qrow < p.Lq) {
         const int64_t base = (int64_t)b * bp.dq_sb + (int64_t)h * bp.dq_sh + (int64_t)qrow * bp.dq_sl;
@@ -395,14 +421,42 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
 // ---------------------------------------------------------------------------
 // dK/dV kernel
 // ---------------------------------------------------------------------------
+// P and dU of this lane's 16 scores (element e: tile row qs0 + (e / 8) * 16 +
+// 8h + e % 8, h = lane / 32), packed to bf16 pairs.  With MASK, rows outside
+// [imin, imax] (the rows that see this lane's key) get 0.
+template <int BIAS, bool MASK>
+__device__ __forceinline__ void dkdv_scores(const FwdParams &p, const f32x16 &s, const f32x16 &dp,
+                                            const f32x4 (&L)[4], const f32x4 (&Dl)[4], int ibase, int key,
+                                            int imin, int imax, float slope_l2, int b, int h, uint32_t (&pk)[8],
+                                            uint32_t (&dk)[8]) {
+    const float dbase = (float)(ibase + (p.Lk - p.Lq) - key);
+    // element offset eo is visible iff (unsigned)(eo - lo) <= span
+    const int lo = imin - ibase;
+    const uint32_t span = (uint32_t)(imax - imin);
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+        float pr[2], du[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int eo = ((e + u) >> 3) * 16 + ((e + u) & 7);
+            du[u] = grad_of_score<BIAS>(p, s[e + u], dp[e + u], L[(e + u) >> 2][(e + u) & 3],
+                                        Dl[(e + u) >> 2][(e + u) & 3], slope_l2, fabsf(dbase + (float)eo),
+                                        dense_bias<BIAS>(p, b, h, ibase + eo, key), &pr[u]);
+            if (MASK && (uint32_t)(eo - lo) > span) pr[u] = du[u] = 0.f;
+        }
+        pk[e >> 1] = pack_bf16x2(pr[0], pr[1]);
+        dk[e >> 1] = pack_bf16x2(du[0], du[1]);
+    }
+}
+
 // 32 query rows (tile rows qs0 .. qs0 + 31, global row i0 + tile row) against
 // this wave's 32 keys.
-template <int D, int BIAS, bool MASK>
+template <int D, int BIAS>
 __device__ __forceinline__ void dkdv_rows(const FwdParams &p, const char *lq, const char *ldo, const float *llse,
                                           const float *ldel, int rbase, int tbase, const u32x4 (&kreg)[D / 16],
                                           const u32x4 (&vreg)[D / 16], f32x16 (&dkacc)[D / 32],
                                           f32x16 (&dvacc)[D / 32], int qs0, int i0, int key, int imin, int imax,
-                                          float slope_l2, int b, int h, int lane) {
+                                          bool masked, float slope_l2, int b, int h, int lane) {
     using C = BwdCfg<D>;
     const int hh = lane >> 5;
     // S = Q K^T, dP = dO V^T (query perm32(r) in matrix-core row r)
@@ -414,7 +468,6 @@ __device__ __forceinline__ void dkdv_rows(const FwdParams &p, const char *lq, co
         s = mfma32(as_bf16x8(load16(lq + ((rbase ^ (ks << 5)) + qs0 * C::RB))), as_bf16x8(kreg[ks]), s);
         dp = mfma32(as_bf16x8(load16(ldo + ((rbase ^ (ks << 5)) + qs0 * C::RB))), as_bf16x8(vreg[ks]), dp);
     }
-    // element e of this lane: tile row qs0 + (e / 8) * 16 + 8 * hh + e % 8
     f32x4 L[4], Dl[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -423,23 +476,13 @@ __device__ __forceinline__ void dkdv_rows(const FwdParams &p, const char *lq, co
         Dl[g] = *reinterpret_cast<const f32x4 *>(ldel + rr);
     }
     const int ibase = i0 + qs0 + hh * 8;
-    const float dbase = (float)(ibase + (p.Lk - p.Lq) - key);
     uint32_t pk[8], dk[8];
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-        float pr[2], du[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int eo = ((e + u) >> 3) * 16 + ((e + u) & 7);
-            const int i = ibase + eo;
-            du[u] = grad_of_score<BIAS>(p, s[e + u], dp[e + u], L[(e + u) >> 2][(e + u) & 3],
-                                        Dl[(e + u) >> 2][(e + u) & 3], slope_l2, fabsf(dbase + (float)eo),
-                                        dense_bias<BIAS>(p, b, h, i, key), &pr[u]);
-            if (MASK && (i < imin || i > imax)) pr[u] = du[u] = 0.f;
-        }
-        pk[e >> 1] = pack_bf16x2(pr[0], pr[1]);
-        dk[e >> 1] = pack_bf16x2(du[0], du[1]);
-    }
+    // the branch covers only the elementwise part, so both paths leave the
+    // accumulators alone (and in the same registers)
+    if (masked)
+        dkdv_scores<BIAS, true>(p, s, dp, L, Dl, ibase, key, imin, imax, slope_l2, b, h, pk, dk);
+    else
+        dkdv_scores<BIAS, false>(p, s, dp, L, Dl, ibase, key, imin, imax, slope_l2, b, h, pk, dk);
     // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -460,20 +503,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
     constexpr int BK = 32 * NW;          // keys per workgroup
     constexpr int BQ = C::BT;            // query rows per streamed tile
     constexpr int T = NW * 64;
-    constexpr int NC = C::TILE / (T * 16);
-    constexpr int RROWS = T * 16 / C::RB;
-    static_assert(NC >= 1 && C::TILE == NC * T * 16, "tile does not split evenly");
-    static_assert(RROWS % 16 == 0, "rounds must keep the swizzle");
     static_assert(NW >= 2, "waves 0 and 1 load the per-row values");
+    // one stage: Q tile, dO tile, LSE (log2 units) and Delta of its BQ rows
+    constexpr int STAGE = 2 * C::TILE + 2 * BQ * 4;
 
-    __shared__ __attribute__((aligned(1024))) char lds_q0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char lds_q1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char lds_o0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) char lds_o1[C::TILE];
-    __shared__ __attribute__((aligned(256))) float lds_l0[BQ];
-    __shared__ __attribute__((aligned(256))) float lds_l1[BQ];
-    __shared__ __attribute__((aligned(256))) float lds_d0[BQ];
-    __shared__ __attribute__((aligned(256))) float lds_d1[BQ];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
     // work item: XCD-contiguous ranges of a head-major list; key tiles in
     // ascending order (under the causal mask the first ones see the most rows)
@@ -539,14 +573,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
     const int tbase = C::tr_base(lane);
     const uint32_t ql_bytes = (uint32_t)p.q_sl * 2u;
     const uint32_t dl_bytes = (uint32_t)bp.do_sl * 2u;
-    uint32_t qgoff, dgoff;
-    {
-        const int pos = wave * 1024 + lane * 16;
-        const int row = pos / C::RB;
-        const int pc = (pos % C::RB) / 16;
-        qgoff = (uint32_t)row * ql_bytes + (uint32_t)((pc ^ C::swz(row)) * 16);
-        dgoff = (uint32_t)row * dl_bytes + (uint32_t)((pc ^ C::swz(row)) * 16);
-    }
+    const uint32_t qgoff = tile_goff<D>(wave, lane, ql_bytes);
+    const uint32_t dgoff = tile_goff<D>(wave, lane, dl_bytes);
+    const uint32_t lds0 = lds_addr(smem);
 
     f32x16 dkacc[C::DB], dvacc[C::DB];
 #pragma unroll
@@ -554,68 +583,50 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) dkacc[db][e] = dvacc[db][e] = 0.f;
 
-    // iteration it: query head hk*G + it / nt, query tile t_first + it % nt
-#define BWD_KV_LOADS(IT_, QL_, OL_, LL_, DL_)                                                                   \
-    do {                                                                                                        \
-        const int hi_ = (IT_) / nt;                                                                             \
-        const int h_ = hk * p.G + hi_;                                                                          \
-        const int q0_ = (t_first + (IT_) - hi_ * nt) * BQ;                                                      \
-        const int nv_ = min(BQ, p.Lq - q0_);                                                                    \
-        BWD_LOAD_TILE(QL_, static_cast<const uint16_t *>(p.q) + (int64_t)b * p.q_sb + (int64_t)h_ * p.q_sh +     \
-                               (int64_t)q0_ * p.q_sl, ql_bytes, nv_, qgoff);                                    \
-        BWD_LOAD_TILE(OL_, static_cast<const uint16_t *>(bp.dout) + (int64_t)b * bp.do_sb +                    \
-                               (int64_t)h_ * bp.do_sh + (int64_t)q0_ * bp.do_sl, dl_bytes, nv_, dgoff);         \
-        const int64_t rw_ = ((int64_t)b * p.Hq + h_) * p.Lq + q0_;                                              \
-        if (wave == 0)                                                                                          \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(bp.lse_l2 + rw_, (uint32_t)nv_ * 4u),           \
-                                                     (__attribute__((address_space(3))) void *)(LL_), 4,        \
-                                                     lane * 4, 0, 0, 0);                                        \
-        if (wave == 1)                                                                                          \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(bp.delta + rw_, (uint32_t)nv_ * 4u),            \
-                                                     (__attribute__((address_space(3))) void *)(DL_), 4,        \
-                                                     lane * 4, 0, 0, 0);                                        \
-    } while (0)
-#define BWD_KV_STEP(MASK_, BUF_, IT_)                                                                           \
-    do {                                                                                                        \
-        const int hi_ = (IT_) / nt;                                                                             \
-        const int h_ = hk * p.G + hi_;                                                                          \
-        const int q0_ = (t_first + (IT_) - hi_ * nt) * BQ;                                                      \
-        const float sl_ = bias_base(BIAS) == kBiasAlibi ? p.slopes[h_] * kLog2e : 0.f;                          \
-        if (!(MASK_) || (wimax >= wimin && q0_ <= wimax && q0_ + BQ - 1 >= wimin)) {                            \
-            _Pragma("unroll 1") for (int sub_ = 0; sub_ < BQ / 32; ++sub_)                                      \
-                dkdv_rows<D, BIAS, MASK_>(p, (BUF_) ? lds_q1 : lds_q0, (BUF_) ? lds_o1 : lds_o0,                \
-                                          (BUF_) ? lds_l1 : lds_l0, (BUF_) ? lds_d1 : lds_d0, rbase, tbase,     \
-                                          kreg, vreg, dkacc, dvacc, sub_ * 32, q0_, key, imin, imax, sl_, b,    \
-                                          h_, lane);                                                            \
-        }                                                                                                       \
-    } while (0)
+    // iteration it: query head hk*G + it / nt, query tile t_first + it % nt,
+    // its tiles in stage it & 1
+    auto issue = [&](int it, int st) {
+        const int hi = it / nt;
+        const int hq = hk * p.G + hi;
+        const int q0 = (t_first + it - hi * nt) * BQ;
+        const int nv = min(BQ, p.Lq - q0);
+        const uint32_t dst = lds0 + st * STAGE;
+        dma_tile<D, T>(static_cast<const uint16_t *>(p.q) + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh +
+                           (int64_t)q0 * p.q_sl, ql_bytes, nv, dst, wave, qgoff);
+        dma_tile<D, T>(static_cast<const uint16_t *>(bp.dout) + (int64_t)b * bp.do_sb + (int64_t)hq * bp.do_sh +
+                           (int64_t)q0 * bp.do_sl, dl_bytes, nv, dst + C::TILE, wave, dgoff);
+        const int64_t rw = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
+        if (wave == 0) dma4(rsrc_words(bp.lse_l2 + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE, lane * 4);
+        if (wave == 1) dma4(rsrc_words(bp.delta + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE + BQ * 4, lane * 4);
+    };
+    auto step = [&](bool masked, int it, int st) {
+        const int hi = it / nt;
+        const int hq = hk * p.G + hi;
+        const int q0 = (t_first + it - hi * nt) * BQ;
+        if (masked && !(wimax >= wimin && q0 <= wimax && q0 + BQ - 1 >= wimin)) return;
+        const float sl = bias_base(BIAS) == kBiasAlibi ? p.slopes[hq] * kLog2e : 0.f;
+        const char *sb = smem + st * STAGE;
+        const float *ll = reinterpret_cast<const float *>(sb + 2 * C::TILE);
+#pragma unroll 1
+        for (int sub = 0; sub < BQ / 32; ++sub) {
+            dkdv_rows<D, BIAS>(p, sb, sb + C::TILE, ll, ll + BQ, rbase, tbase, kreg, vreg, dkacc, dvacc, sub * 32,
+                               q0, key, imin, imax, masked, sl, b, hq, lane);
+        }
+    };
 
     if (iters > 0) {
-        BWD_KV_LOADS(0, lds_q0, lds_o0, lds_l0, lds_d0);
-        wait_vmem();
+        issue(0, 0);
+        wait_all_loads();
         __syncthreads();
     }
     for (int it = 0; it < iters; ++it) {
+        const int st = it & 1;
+        if (it + 1 < iters) issue(it + 1, st ^ 1);
         const int tq = t_first + it % nt;
-        const bool masked = tq < u_first || tq >= u_end;
-        if ((it & 1) == 0) {
-            if (it + 1 < iters) BWD_KV_LOADS(it + 1, lds_q1, lds_o1, lds_l1, lds_d1);
-            if (masked)
-                BWD_KV_STEP(true, 0, it);
-            else
-                BWD_KV_STEP(false, 0, it);
-        } else {
-            if (it + 1 < iters) BWD_KV_LOADS(it + 1, lds_q0, lds_o0, lds_l0, lds_d0);
-            if (masked)
-                BWD_KV_STEP(true, 1, it);
-            else
-                BWD_KV_STEP(false, 1, it);
-        }
-        wait_vmem();
+        step(tq < u_first || tq >= u_end, it, st);
+        wait_all_loads();
         __syncthreads();
     }
-#undef BWD_KV_STEP
-#undef BWD_KV_LOADS
 
     if (key < p.Lk) {
         const int64_t kb = (int64_t)b * bp.dk_sb + (int64_t)hk * bp.dk_sh + (int64_t)key * bp.dk_sl;

@@ -80,3 +80,12 @@ def test_workload_counts():
     assert round(bench.attention_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, True) / 1e9, 2) == 2199.09
     w = synth.C4_DECODE
     assert bench.decode_step_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, 32) == 2_164_787_200
+
+
+def test_backward_flops_are_five_products():
+    # five products of 2*d FLOP per visible pair: 2.5 times the forward's two
+    for causal, window in ((False, None), (True, None), (True, (7, -1))):
+        f = bench.attention_flops(2, 3, 40, 50, 64, causal, window)
+        b = bench.backward_flops(2, 3, 40, 50, 64, causal, window)
+        assert 2 * b == 5 * f
+    assert bench.backward_flops(4, 32, 4096, 4096, 128, False) == 10 * 128 * 4 * 32 * 4096 * 4096

@@ -1,10 +1,11 @@
 """Checks on the gfx950 code the compiler makes from the kernel sources (CPU
 only: hipcc cross-compiles, nothing runs).
 
-The decode kernel issues its buffer-to-LDS loads from inline assembly that
-writes M0 itself; that is only sound while no compiler-generated instruction
-of that file reads or writes M0.  Both kernels must also run without scratch
-(register spills) in every instantiation."""
+The decode and backward kernels issue their buffer-to-LDS loads from inline
+assembly that writes M0 itself; that is only sound while no compiler-generated
+instruction of those files reads or writes M0.  The kernels must also run
+without scratch (register spills) in every instantiation, and the dK/dV loop
+must not shuffle its accumulators between registers."""
 import os
 import re
 import shutil
@@ -44,8 +45,9 @@ def compiler_lines(asm):
 
 
 @needs_hipcc
-def test_decode_m0_only_in_inline_asm(tmp_path):
-    asm = device_asm("decode_bf16.hip", tmp_path)
+@pytest.mark.parametrize("src", ["decode_bf16.hip", "bwd_bf16.hip"])
+def test_m0_only_in_inline_asm(src, tmp_path):
+    asm = device_asm(src, tmp_path)
     bad = [s for s in compiler_lines(asm) if re.search(r"\bm0\b", s)]
     assert not bad, bad[:5]
     # and the inline assembly does set it before each buffer-to-LDS load
@@ -53,8 +55,33 @@ def test_decode_m0_only_in_inline_asm(tmp_path):
 
 
 @needs_hipcc
-@pytest.mark.parametrize("src", ["decode_bf16.hip", "prefill_bf16.hip"])
+@pytest.mark.parametrize("src", ["decode_bf16.hip", "prefill_bf16.hip", "bwd_bf16.hip"])
 def test_no_scratch(src, tmp_path):
     asm = device_asm(src, tmp_path)
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", asm)]
     assert sizes and max(sizes) == 0, sizes
+
+
+@needs_hipcc
+def test_dkdv_loop_keeps_accumulators_in_place(tmp_path):
+    """Accumulator-to-accumulator register moves (v_accvgpr_mov) appear in the
+    dK/dV kernel only where it zeroes its accumulators (one v_accvgpr_write of
+    0, copied to the others), never next to matrix-core work."""
+    asm = device_asm("bwd_bf16.hip", tmp_path)
+    kernels = list(re.finditer(r"^(_ZN4attn\w*bwd_dkdv_kernel\w*):", asm, flags=re.M))
+    assert kernels
+    for m in kernels:
+        body = asm[m.end():asm.index("s_endpgm", m.end())]
+        for blk in re.split(r"^\.LBB\d+_\d+:", body, flags=re.M):
+            if "v_accvgpr_mov" not in blk:
+                continue
+            assert "v_mfma" not in blk, m.group(1)
+            zero = set()
+            for ln in blk.splitlines():
+                w = re.search(r"v_accvgpr_write_b32 (a\d+), 0\b", ln)
+                if w:
+                    zero.add(w.group(1))
+                mv = re.search(r"v_accvgpr_mov_b32 (a\d+), (a\d+)", ln)
+                if mv:
+                    assert mv.group(2) in zero, (m.group(1), ln.strip())   # copies a zero
+                    zero.add(mv.group(1))
