@@ -93,3 +93,38 @@ def test_tiny_reference_workload():
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), w.causal)
     assert float(np.max(np.abs(o.cpu().double().numpy() - O_ref))) <= 1e-5
     assert float(np.max(np.abs(lse.cpu().double().numpy() - L_ref))) <= 1e-5
+
+
+@pytest.mark.parametrize("w", [synth.BWD_PREFILL, synth.C2_CAUSAL], ids=lambda w: w.name)
+def test_backward_fullsize_sampled_heads(w):
+    """attn_bwd on the whole workload (bf16 gradients, as bench.py times it);
+    four (b, h) heads compared in full (every row of dQ, every key of dK, dV)
+    with the oracle's gradients of those heads, under the tolerances of the
+    small-size backward tests (max |err| <= 2e-2 * max |ref|, relative
+    Frobenius error <= 8e-3)."""
+    print("full-size backward", w.name, flush=True)
+    assert w.Hq == w.Hkv
+    q, k, v = synth.make_qkv(w, device="cuda")
+    do = synth.make_dout(w, device="cuda")
+    scale = w.softmax_scale()
+    o, lse = attn.attn_fwd_prefill(q, k, v, scale, w.causal)
+    dq, dk, dv = attn.attn_bwd(q, k, v, o, lse, do, scale, w.causal)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    rng = np.random.default_rng(w.seed)
+    heads = [(0, 0), (w.B - 1, w.Hq - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(2)]
+    # the heads are independent: stack them as a batch of one-head problems
+    pick = lambda t: torch.stack([t[b, h] for b, h in heads]).unsqueeze(1).float().cpu()
+    refs = oracle.attention_bwd(pick(q), pick(k), pick(v), pick(do), scale, w.causal, threads=len(heads))
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        g = pick(got).numpy().astype(np.float64)
+        for n, (b, h) in enumerate(heads):
+            scale_ref = float(np.max(np.abs(ref[n])))
+            err = np.abs(g[n] - ref[n])
+            mx = float(np.max(err)) / scale_ref
+            fro = float(np.linalg.norm(err) / np.linalg.norm(ref[n]))
+            assert mx <= 2e-2 and fro <= 8e-3, "%s %s b=%d h=%d: max %.3e fro %.3e" % (w.name, name, b, h, mx, fro)
+        print("%s %s: max|err|/max|ref| <= %.2e" % (w.name, name, max(
+            float(np.max(np.abs(g[n] - ref[n]))) / float(np.max(np.abs(ref[n]))) for n in range(len(heads)))),
+            flush=True)
