@@ -16,6 +16,11 @@ Default run (N = 1):
     at L=4096, with the forward's O and LSE as inputs.  Reported under
     "backward" in algorithmic TFLOP/s: 10 * d FLOP per visible pair (the five
     products S, dP, dV, dK, dQ), recomputation not counted.
+  * plan leg -- attn_fwd (automatic choice of parallel dimensions) on a
+    short-query GQA shape (B=1, Hq=32, Hkv=8, Lq=16, Lk=32768): the plan it
+    picks, its time, and the prefill kernel's time on the same problem.
+    Reported under "plan".  `--plan-sweep` times both paths over the shape
+    grid that set the planner's boundary (one JSON line per shape).
   * cpu_baseline -- the fp64 oracle, timed on the host cores on a bounded
     sample of the prefill workload (whole heads), scaled to TFLOP/s.
 
@@ -282,6 +287,91 @@ def time_backward(w, steps, warmup, warm_s=1.0):
     return wall, avg_ms * 1e-3, flops
 
 
+def _median_us(fn, reps=10):
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    d = sorted(a.elapsed_time(b) for a, b in ev)
+    return d[len(d) // 2] * 1e3
+
+
+def time_plan(w):
+    """attn_fwd with its plan against the prefill kernel on the same problem."""
+    import torch
+    import synth
+    import online_softmax_fusion_amd as attn
+
+    q, k, v = synth.make_qkv(w, device="cuda")
+    sc = w.softmax_scale()
+    plan = attn.attn_fwd_choose_plan(q, k, v, sc, w.causal)
+    ws = torch.empty((max(plan.workspace_bytes, 16),), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
+    t_fwd = _median_us(lambda: attn.attn_fwd(q, k, v, sc, w.causal, out=o, lse=lse, workspace=ws), 20)
+    t_pf = _median_us(lambda: attn.attn_fwd_prefill(q, k, v, sc, w.causal, out=o, lse=lse), 20)
+    log("plan: %s -> %s S=%d, %.1f us (prefill kernel %.1f us)" %
+        (w.name, "split-K" if plan.method == attn.ATTN_PLAN_SPLITK else "prefill", plan.num_splits, t_fwd, t_pf))
+    return {"workload": w.name, "method": "splitk" if plan.method == attn.ATTN_PLAN_SPLITK else "prefill",
+            "splits": plan.num_splits, "attn_fwd_us": round(t_fwd, 1), "prefill_kernel_us": round(t_pf, 1),
+            "speedup": round(t_pf / t_fwd, 2)}
+
+
+def plan_sweep(causal):
+    """Both forward paths over B 1, 4; Hq/Hkv 8/8, 32/8, 64/8; Lq 1..2048;
+    Lk 4096, 32768 (d = 128, bf16): prefill kernel, split-K at each split
+    count, the planner's choice.  One JSON line per shape on stdout."""
+    import torch
+    import synth
+    import online_softmax_fusion_amd as attn
+
+    cu = attn.attn_device_cu_count(0)
+    for Lk in (4096, 32768):
+        for B in (1, 4):
+            for Hq, Hkv in ((8, 8), (32, 8), (64, 8)):
+                w = synth.Workload("sweep", B, Hq, Hkv, 1, Lk, 128, "bf16", causal, "none", 5)
+                _, k, v = synth.make_qkv(w, device="cuda")
+                for Lq in (1, 4, 16, 64, 128, 256, 512, 1024, 2048):
+                    q = synth.normal((B, Hq, Lq, 128), 5, 0, "bf16", "cuda")
+                    sc = w.softmax_scale()
+                    o = torch.empty_like(q)
+                    lse = torch.empty((B, Hq, Lq), device="cuda")
+                    res = {"B": B, "Hq": Hq, "Hkv": Hkv, "Lq": Lq, "Lk": Lk, "causal": causal,
+                           "prefill_us": round(_median_us(lambda: attn.attn_fwd_prefill(q, k, v, sc, causal, out=o,
+                                                                                       lse=lse)), 1)}
+                    blocks = B * Hkv * ((Hq // Hkv * Lq + 31) // 32)
+                    best = None
+                    for S in (1, 2, 4, 8, 16, 32, 64, 128):
+                        if S > max(1, Lk // 256) or (S > 1 and blocks * S > 8 * cu):
+                            continue
+                        op = torch.empty((B, Hq, Lq, S, 128), device="cuda")
+                        mp = torch.empty((B, Hq, Lq, S), device="cuda")
+                        lp = torch.empty_like(mp)
+
+                        def run():
+                            attn.attn_fwd_decode_splitk(q, k, v, S, sc, causal, o_part=op, m_part=mp, l_part=lp)
+                            attn.attn_splitk_combine(op, mp, lp, out=o, lse=lse)
+
+                        t = _median_us(run)
+                        res["splitk_S%d_us" % S] = round(t, 1)
+                        if best is None or t < best[1]:
+                            best = (S, t)
+                    res["best_S"], res["best_splitk_us"] = best[0], round(best[1], 1)
+                    plan = attn.attn_fwd_choose_plan(q, k, v, sc, causal)
+                    res["plan"] = "splitk" if plan.method == attn.ATTN_PLAN_SPLITK else "prefill"
+                    res["plan_S"] = plan.num_splits
+                    print(json.dumps(res), flush=True)
+                del k, v
+                torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle as it stands, on whole heads of the prefill workload."""
     import numpy as np
@@ -384,6 +474,8 @@ def main():
     ap.add_argument("--backward", default=None,
                     help="backward workload name (default: non-causal B4 H32 L4096), or 'none' to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plan-sweep", choices=("causal", "noncausal"), default=None,
+                    help="only time both forward paths over the planner's shape grid (JSON lines)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -419,6 +511,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 3}))
         return
     attn.load_library()
+    if args.plan_sweep:
+        plan_sweep(args.plan_sweep == "causal")
+        return
     wp = synth.WORKLOADS[args.prefill] if args.prefill else synth.C2_CAUSAL
     wd = synth.WORKLOADS[args.decode] if args.decode else synth.C4_DECODE
     if args.splits:
@@ -427,6 +522,7 @@ def main():
     torch.cuda.synchronize()
     step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup, args.warm_seconds)
     d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup, args.warm_seconds)
+    plan_res = time_plan(synth.PLAN_SHORT_GQA)
     wb = None if args.backward == "none" else synth.WORKLOADS[args.backward or synth.BWD_PREFILL.name]
     if wb is not None:
         b_step_s, b_kern_s, b_flops = time_backward(wb, args.steps, args.warmup, args.warm_seconds)
@@ -464,6 +560,7 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_kern_gbs / HBM_PEAK_GBS, 4),
                                 "traffic": measured_traffic("decode_bf16_kernel", wd.name, DECODE_SOURCES)}},
     }
+    result["plan"] = plan_res
     if wb is not None:
         b_kern_tflops = b_flops / b_kern_s / 1e12
         result["backward"] = {

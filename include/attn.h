@@ -168,6 +168,57 @@ attn_status attn_splitk_combine(const float *o_part, const float *m_part, const 
 int32_t attn_decode_choose_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
                                   int32_t cu_count);
 
+/*
+ * Automatic choice of the parallel dimensions
+ * -------------------------------------------
+ * The prefill kernel parallelises over batch, query head and query rows (one
+ * workgroup per 128 rows of one query head, every K/V tile streamed past
+ * it); the split-K kernel parallelises over batch, K/V head, the rows of a
+ * K/V group (the G query heads of the group times Lq rows, stacked 32 to a
+ * workgroup, so each K/V element is read once per group) and key chunks,
+ * followed by the combine.  The Mirage lecture notes (section 7.1) observe
+ * that fixed choices of these dimensions underfill the GPU for few heads and
+ * short query lengths, and that the right choice depends on the problem; the
+ * Neptune notes (section 6) trade partial-result storage for parallelism
+ * along the keys.
+ *
+ * attn_fwd_choose_plan picks, from the shapes alone (pure host function):
+ *   split-K, when R = B * Hkv * ceil(G * Lq / 32) row blocks fit on the
+ *            compute units at once (R <= cu_count), with num_splits from
+ *            attn_decode_choose_splits;
+ *   prefill, otherwise (and always for fp32 inputs, or shapes the split-K
+ *            grid cannot hold).
+ * The boundary is measured: on MI355X, over 216 shapes (B 1 and 4; Hq/Hkv
+ * 8/8, 32/8, 64/8; Lq 1 to 2048; Lk 4096 and 32768; causal and not) the
+ * split-K path is faster in every shape with R <= 256 (1.3x to 16.6x) and
+ * slower in every shape with R >= 512 (by 1.1x to 3x).
+ */
+enum { ATTN_PLAN_PREFILL = 0, ATTN_PLAN_SPLITK = 1 };
+
+typedef struct attn_fwd_plan {
+    int32_t method;                  /* ATTN_PLAN_PREFILL or ATTN_PLAN_SPLITK */
+    int32_t num_splits;              /* split-K: key chunks (1 = grouped rows, no split); prefill: 0 */
+    size_t workspace_bytes;          /* device workspace attn_fwd needs for this plan (0 for prefill) */
+} attn_fwd_plan;
+
+/*
+ * attn_fwd_choose_plan -- the plan attn_fwd runs for `a` on a device with
+ * cu_count compute units (<= 0: 256).  Validates like attn_validate_prefill
+ * and writes *plan on success.
+ */
+attn_status attn_fwd_choose_plan(const attn_fwd_args *a, int32_t cu_count, attn_fwd_plan *plan);
+
+/*
+ * attn_fwd -- the forward with the plan chosen for the current device: writes
+ * o and, when lse != NULL, lse, exactly as attn_fwd_prefill does (same
+ * arguments and conventions).  A split-K plan keeps its partials in the
+ * caller's device workspace (16-byte aligned, at least plan.workspace_bytes;
+ * its contents on entry do not matter); a smaller workspace returns
+ * ATTN_ERR_WORKSPACE and enqueues nothing.  NULL / 0 is fine when the plan is
+ * prefill.
+ */
+attn_status attn_fwd(const attn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream);
+
 /* attn_decode_partial_bytes -- bytes of o_part + m_part + l_part for a decode call. */
 size_t attn_decode_partial_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int32_t num_splits);
 

@@ -9,6 +9,8 @@ Entry points (same names as the C ABI):
     attn_fwd_prefill(q, k, v, ...)             -> (o, lse)
     attn_fwd_decode_splitk(q, k, v, splits, ...) -> (o_part, m_part, l_part)
     attn_splitk_combine(o_part, m_part, l_part, ...) -> (o, lse)
+    attn_fwd(q, k, v, ...)                     -> (o, lse)   (planned: prefill or split-K)
+    attn_fwd_choose_plan(q, k, v, ...)         -> AttnFwdPlan
     attn_bwd(q, k, v, o, lse, dout, ...)       -> (dq, dk, dv)
 and the conveniences ``prefill`` (= attn_fwd_prefill) and ``decode`` (split-K
 local step followed by the combine on the same stream).
@@ -26,7 +28,8 @@ __all__ = [
     "AttnError", "load_library", "library_path", "attn_fwd_prefill", "attn_fwd_decode_splitk",
     "attn_splitk_combine", "attn_decode_choose_splits", "attn_decode_partial_bytes",
     "attn_device_cu_count", "prefill", "decode", "chunk_length", "AttnFwdArgs", "AttnBwdArgs", "attn_bwd",
-    "attn_bwd_workspace_bytes",
+    "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_choose_plan", "AttnFwdPlan", "ATTN_PLAN_PREFILL",
+    "ATTN_PLAN_SPLITK",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +39,7 @@ _LIB = None
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, 1, 2, 3, 4
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_BIAS_NONE, ATTN_BIAS_DENSE, ATTN_BIAS_ALIBI = 0, 1, 2
+ATTN_PLAN_PREFILL, ATTN_PLAN_SPLITK = 0, 1
 
 _I64x3 = ctypes.c_int64 * 3
 _I64x4 = ctypes.c_int64 * 4
@@ -56,6 +60,11 @@ class AttnFwdArgs(ctypes.Structure):
         ("softcap", ctypes.c_float), ("window", ctypes.c_int32),
         ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
     ]
+
+
+class AttnFwdPlan(ctypes.Structure):
+    """Mirror of ``attn_fwd_plan`` in include/attn.h."""
+    _fields_ = [("method", ctypes.c_int32), ("num_splits", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class AttnBwdArgs(ctypes.Structure):
@@ -115,6 +124,10 @@ def load_library():
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_fwd_args_size.argtypes = []
     lib.attn_fwd_args_size.restype = ctypes.c_size_t
+    lib.attn_fwd_choose_plan.argtypes = [P, i32, ctypes.POINTER(AttnFwdPlan)]
+    lib.attn_fwd_choose_plan.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [P, vp, ctypes.c_size_t, vp]
+    lib.attn_fwd.restype = ctypes.c_int
     PB = ctypes.POINTER(AttnBwdArgs)
     lib.attn_bwd.argtypes = [PB, vp]
     lib.attn_bwd.restype = ctypes.c_int
@@ -393,3 +406,55 @@ def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool 
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_fwd_choose_plan(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bias=None,
+                         alibi_slopes=None, softcap: float = 0.0, window: Optional[Tuple[int, int]] = None,
+                         cu_count: int = 0, out_dtype: Optional[torch.dtype] = None) -> AttnFwdPlan:
+    """The plan (prefill or split-K with its split count and workspace size)
+    attn_fwd would run for these arguments on a device with ``cu_count``
+    compute units (0: the current device's)."""
+    lib = load_library()
+    if cu_count <= 0:
+        cu_count = attn_device_cu_count(q.device.index or 0)
+    out = torch.empty((1,), dtype=out_dtype or q.dtype, device=q.device)
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, None, None, softcap, window)
+    a.o, a.o_dtype = out.data_ptr(), _dtype_code(out.dtype)
+    B, Hq, Lq, D = q.shape
+    a.o_strides = _I64x3(Hq * Lq * D, Lq * D, D)
+    plan = AttnFwdPlan()
+    st = lib.attn_fwd_choose_plan(ctypes.byref(a), int(cu_count), ctypes.byref(plan))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_choose_plan")
+    return plan
+
+
+def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bias=None, alibi_slopes=None,
+             out=None, out_dtype: Optional[torch.dtype] = None, lse=None, return_lse: bool = True,
+             softcap: float = 0.0, window: Optional[Tuple[int, int]] = None, workspace=None):
+    """Forward with the automatically chosen parallel dimensions (prefill, or
+    grouped split-K plus combine).  Same arguments and results as
+    ``attn_fwd_prefill``; ``workspace`` may be a GPU byte tensor to reuse (a
+    new one of the plan's size is allocated otherwise)."""
+    lib = load_library()
+    B, Hq, Lq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _check_4d("out", out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq * Lq):
+        raise ValueError("lse must be a contiguous fp32 tensor of B*Hq*Lq elements")
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, out, lse, softcap, window)
+    plan = AttnFwdPlan()
+    st = lib.attn_fwd_choose_plan(ctypes.byref(a), attn_device_cu_count(q.device.index or 0), ctypes.byref(plan))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_choose_plan")
+    if workspace is None and plan.workspace_bytes > 0:
+        workspace = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return out, lse

@@ -278,6 +278,48 @@ attn_status attn_validate_bwd(const attn_bwd_args *a) {
     return ATTN_OK;
 }
 
+attn_status attn_fwd_choose_plan(const attn_fwd_args *a, int32_t cu_count, attn_fwd_plan *plan) {
+    if (plan == nullptr) return ATTN_ERR_INVALID_ARG;
+    attn_status st = attn_validate_prefill(a);
+    if (st != ATTN_OK) return st;
+    const int64_t cu = cu_count > 0 ? cu_count : 256;
+    const int64_t G = a->Hq / a->Hkv;
+    const int64_t rblocks = (G * a->Lq + 31) / 32;
+    const int64_t R = a->B * a->Hkv * rblocks;
+    plan->method = ATTN_PLAN_PREFILL;
+    plan->num_splits = 0;
+    plan->workspace_bytes = 0;
+    if (a->dtype == ATTN_BF16 && R > 0 && R <= cu && a->Lk > 0 && a->B * a->Hkv <= 65535 && rblocks <= 65535) {
+        const int32_t S = attn_decode_choose_splits(a->B, a->Hq, a->Hkv, a->Lq, a->Lk, (int32_t)cu);
+        plan->method = ATTN_PLAN_SPLITK;
+        plan->num_splits = S;
+        plan->workspace_bytes = attn_decode_partial_bytes(a->B, a->Hq, a->Lq, a->D, S);
+    }
+    return ATTN_OK;
+}
+
+attn_status attn_fwd(const attn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+    attn_status st = attn_validate_prefill(a);
+    if (st != ATTN_OK) return st;
+    if (a->B * a->Hq * a->Lq == 0) return ATTN_OK;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    attn_fwd_plan plan;
+    st = attn_fwd_choose_plan(a, attn_device_cu_count(device), &plan);
+    if (st != ATTN_OK) return st;
+    if (plan.method == ATTN_PLAN_PREFILL) return attn_fwd_prefill(a, stream);
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
+    const int64_t parts = a->B * a->Hq * a->Lq * (int64_t)plan.num_splits;
+    float *o_part = static_cast<float *>(workspace);
+    float *m_part = o_part + parts * a->D;
+    float *l_part = m_part + parts;
+    st = attn_fwd_decode_splitk(a, plan.num_splits, o_part, m_part, l_part, stream);
+    if (st != ATTN_OK) return st;
+    return attn_splitk_combine(o_part, m_part, l_part, a->B, a->Hq, a->Lq, a->D, plan.num_splits, a->o, a->o_dtype,
+                               a->o_strides, a->lse, stream);
+}
+
 attn_status attn_bwd(const attn_bwd_args *a, void *stream) {
     attn_status st = attn_validate_bwd(a);
     if (st != ATTN_OK) return st;

@@ -88,8 +88,14 @@ WINDOW_PREFILL = Workload("window4096-causal-prefill-bf16-B1-H8-L32768-d128", 1,
 BWD_PREFILL = Workload("bwd-noncausal-bf16-B4-H32-L4096-d128", 4, 32, 32, 4096, 4096, 128,
                        "bf16", False, "none", 1008)
 
+# A short-query GQA forward (16 new rows against a 32768-key cache, the group
+# sizes of the Mirage lecture's GQA case, section 7.1, with 8 K/V heads): the
+# shape where the choice of parallel dimensions matters most.
+PLAN_SHORT_GQA = Workload("short-gqa-bf16-B1-Hq32-Hkv8-Lq16-Lk32768-d128", 1, 32, 8, 16, 32768, 128,
+                          "bf16", True, "none", 1009)
+
 WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PREFILL, C5_DECODE,
-                                 SOFTCAP_PREFILL, WINDOW_PREFILL, BWD_PREFILL)}
+                                 SOFTCAP_PREFILL, WINDOW_PREFILL, BWD_PREFILL, PLAN_SHORT_GQA)}
 
 
 def torch_dtype(name: str) -> torch.dtype:
