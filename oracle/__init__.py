@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for fused attention forward and the split-K combine.
+"""fp64 CPU oracle for fused attention (forward, split-K combine, gradients)
+and for the row-wise L2 norm.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
@@ -54,6 +55,8 @@ def load_path(path: str):
                                          dbl, ctypes.c_int, i64, i64,
                                          ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     lib.oracle_attention_bwd.restype = ctypes.c_int
+    lib.oracle_l2norm.argtypes = [i64, i64, vp, i64, vp, vp]
+    lib.oracle_l2norm.restype = ctypes.c_int
     return lib
 
 
@@ -195,3 +198,19 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool = False, *, bias=Non
     if rc != 0:
         raise ValueError("oracle_attention_bwd rejected its arguments (rc=%d)" % rc)
     return dq, dk, dv
+
+
+def l2norm(x, lib=None):
+    """fp64 (y [rows, H], norm [rows]) of the rows of the 2-D array ``x``:
+    norm = sqrt(sum x^2), y = x / norm (0 for a zero row)."""
+    lib = lib or load()
+    xa = _f32(x)
+    if xa.ndim != 2:
+        raise ValueError("x must be 2-D [rows, H]")
+    rows, H = xa.shape
+    y = np.zeros((rows, H), dtype=np.float64)
+    n = np.zeros((rows,), dtype=np.float64)
+    rc = lib.oracle_l2norm(rows, H, _ptr(xa), H, _ptr(y), _ptr(n))
+    if rc != 0:
+        raise ValueError("oracle_l2norm rejected its arguments")
+    return y, n

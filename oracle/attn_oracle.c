@@ -504,3 +504,32 @@ int oracle_attention_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t
     pthread_mutex_destroy(&J->lock);
     return rc;
 }
+
+/*
+ * oracle_l2norm: the Euclidean norm of each row and the row divided by it,
+ * in fp64:
+ *   norm_i = sqrt(sum_j x_ij^2),   y_ij = x_ij / norm_i   (y = 0 for a zero row).
+ * The [Neptune notes] list the numerically stable L2 norm among the
+ * reductions their repair algebra fuses (section 4, and the non-attention
+ * operators of section 9); this is the plain definition that any fused or
+ * split form must reach.  In fp64 the squares of every finite fp32 value are
+ * finite and normal, so the definition needs no scaling here.
+ * x: rows x H fp32, row r at x + r * x_stride.  y: rows x H fp64 (contiguous)
+ * or NULL; norm: rows fp64 or NULL.  Returns 0 or -1 (invalid argument).
+ */
+int oracle_l2norm(int64_t rows, int64_t H, const float *x, int64_t x_stride, double *y, double *norm)
+{
+    if (rows < 0 || H < 0 || x_stride < H) return -1;
+    if (rows * H > 0 && !x) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * x_stride;
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) ss += (double)xr[j] * (double)xr[j];
+        const double n = sqrt(ss);
+        if (norm) norm[r] = n;
+        if (y) {
+            for (int64_t j = 0; j < H; ++j) y[r * H + j] = n > 0.0 ? (double)xr[j] / n : 0.0;
+        }
+    }
+    return 0;
+}

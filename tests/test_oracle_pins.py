@@ -24,6 +24,9 @@ The oracle is checked against things other than itself:
   brute force, and invariants: value gradients add up to the output gradients,
   key gradients add up to zero, equal keys give dQ = 0, Q = 0 gives dV in
   closed form;
+* the row L2 norm: closed forms (3-4-5 at scales 2^100 and 2^-120, ones),
+  exact power-of-two scale invariance, unit rows, zero rows, a strided input,
+  numpy.linalg.norm on random rows;
 * planted mistakes: copies of the oracle with a plausible error each (wrong kv
   head, dropped scale, bias sign, causal off-by-one, log base, combine weight,
   dropped Delta, missing cap slope, wrong head group in the backward, ...)
@@ -790,6 +793,64 @@ def test_bwd_thread_count_does_not_matter():
 
 
 # ----------------------------------------------------------------------------
+# row L2 norm (Neptune notes section 4 lists the numerically stable L2 norm
+# among the reductions the repair algebra fuses): the plain definition
+# ----------------------------------------------------------------------------
+def _l2_strided(lib, x, stride):
+    """call the oracle on rows `stride` floats apart (padding filled with 7s)"""
+    import ctypes
+    rows, H = x.shape
+    buf = np.full((rows, stride), 7.0, np.float32)
+    buf[:, :H] = x
+    y = np.zeros((rows, H), np.float64)
+    n = np.zeros((rows,), np.float64)
+    rc = lib.oracle_l2norm(rows, H, buf.ctypes.data, stride, y.ctypes.data, n.ctypes.data)
+    assert rc == 0
+    return y, n
+
+
+def check_l2norm_pins(lib=None):
+    lib = lib or oracle.load()
+    # 3-4-5 triangle, exact at any power-of-two scale (squares stay normal in fp64)
+    for k in (0, 100, -120):
+        x = np.array([[3.0 * 2.0 ** k, 4.0 * 2.0 ** k]], np.float32)
+        y, n = oracle.l2norm(x, lib=lib)
+        assert n[0] == 5.0 * 2.0 ** k, (k, n[0])
+        assert y[0, 0] == 3.0 / 5.0 and y[0, 1] == 4.0 / 5.0
+    # a row of ones has norm sqrt(H)
+    for H in (1, 7, 4096):
+        y, n = oracle.l2norm(np.ones((1, H), np.float32), lib=lib)
+        assert n[0] == math.sqrt(H)
+        assert np.all(np.abs(y - 1.0 / math.sqrt(H)) <= 1e-16)
+    # zero row: norm 0, y = 0; one nonzero entry: y = +-1 there
+    x = np.zeros((2, 9), np.float32)
+    x[1, 4] = -2.5
+    y, n = oracle.l2norm(x, lib=lib)
+    assert n[0] == 0.0 and np.all(y[0] == 0.0)
+    assert n[1] == 2.5 and y[1, 4] == -1.0 and np.count_nonzero(y[1]) == 1
+    # scaling by 2^k scales the norm by 2^k exactly and leaves y unchanged
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((5, 300)).astype(np.float32)
+    y0, n0 = oracle.l2norm(x, lib=lib)
+    for k in (60, -60):
+        y1, n1 = oracle.l2norm((x * np.float32(2.0 ** k)).astype(np.float32), lib=lib)
+        assert np.array_equal(n1, n0 * 2.0 ** k) and np.array_equal(y1, y0)
+    # against numpy's norm on random rows of several magnitudes; unit rows
+    x = (rng.standard_normal((6, 1000)) * np.array([1e-20, 1e-3, 1, 1e3, 1e15, 1e30])[:, None]).astype(np.float32)
+    y, n = oracle.l2norm(x, lib=lib)
+    ref = np.linalg.norm(x.astype(np.float64), axis=1)
+    assert np.all(np.abs(n - ref) <= 1e-14 * ref)
+    assert np.all(np.abs(np.sum(y * y, axis=1) - 1.0) <= 1e-13)
+    # rows `stride` floats apart
+    ys, ns = _l2_strided(lib, x, 1003)
+    assert np.array_equal(ns, n) and np.array_equal(ys, y)
+
+
+def test_l2norm_pins():
+    check_l2norm_pins()
+
+
+# ----------------------------------------------------------------------------
 # planted mistakes must be caught
 # ----------------------------------------------------------------------------
 CAP_THEN_BIAS = """        if (J->softcap > 0.0) {
@@ -846,6 +907,12 @@ MUTANTS = {
     "bwd_heads_interleaved": ("for (int64_t h = hk * G; h < (hk + 1) * G; ++h) {",
                               "for (int64_t h = hk; h < J->Hq; h += J->Hkv) {"),
     "bwd_unnormalised_p": ("s[j - jlo] = exp(s[j - jlo] - m) / l;", "s[j - jlo] = exp(s[j - jlo] - m);"),
+    # row L2 norm
+    "l2_missing_sqrt": ("const double n = sqrt(ss);", "const double n = ss;"),
+    "l2_sum_of_abs": ("ss += (double)xr[j] * (double)xr[j];", "ss += fabs((double)xr[j]);"),
+    "l2_zero_row_nan": ("n > 0.0 ? (double)xr[j] / n : 0.0", "(double)xr[j] / n"),
+    "l2_divides_by_square": ("n > 0.0 ? (double)xr[j] / n : 0.0", "n > 0.0 ? (double)xr[j] / (n * n) : 0.0"),
+    "l2_stride_ignored": ("const float *xr = x + r * x_stride;", "const float *xr = x + r * H;"),
     "lse_log2": ("*lse = m + log(l);", "*lse = m + log2(l);"),
     "missing_normalise": ("for (int64_t d = 0; d < D; ++d) o[d] /= l;", ";"),
     "combine_weight_sign": ("const double w = exp(ms - M);", "const double w = exp(M - ms);"),
@@ -892,6 +959,7 @@ def _pin_suite(lib):
         assert_close(lc, lse, 1e-6, "combine LSE")
         for case in BWD_CASES:
             check_bwd_finite_differences(case, lib=lib, elems=12)
+        check_l2norm_pins(lib)
     except AssertionError:
         return False
     return True
