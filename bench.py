@@ -21,6 +21,10 @@ Default run (N = 1):
     picks, its time, and the prefill kernel's time on the same problem.
     Reported under "plan".  `--plan-sweep` times both paths over the shape
     grid that set the planner's boundary (one JSON line per shape).
+  * l2norm leg -- the row L2 norm (the same repair algebra on a sum of
+    squares): 32768 rows of 4096 bf16 values in one pass, and 8 rows of
+    4194304 fp32 values split over the row.  Reported under "l2norm" in
+    algorithmic GB/s (x read once, y and the norms written once).
   * cpu_baseline -- the fp64 oracle, timed on the host cores on a bounded
     sample of the prefill workload (whole heads), scaled to TFLOP/s.
 
@@ -303,6 +307,51 @@ def _median_us(fn, reps=10):
     return d[len(d) // 2] * 1e3
 
 
+def l2norm_bytes(rows, H, elem_x, elem_y) -> int:
+    """x read once, y written once, one fp32 norm per row."""
+    return rows * H * (elem_x + elem_y) + rows * 4
+
+
+def time_l2norm(w, steps, warmup, warm_s=1.0):
+    """One step = one l2norm_rows call (one or two kernels) on resident rows."""
+    import torch
+    import synth
+    import online_softmax_fusion_amd as attn
+
+    x = synth.make_rows(w, device="cuda")
+    S = attn.l2norm_choose_splits(w.rows, w.H, x.dtype, attn.attn_device_cu_count(0))
+    y = torch.empty_like(x)
+    n = torch.empty((w.rows,), dtype=torch.float32, device="cuda")
+    ws = torch.empty((max(attn.l2norm_workspace_bytes(w.rows, S), 16),), dtype=torch.uint8, device="cuda")
+
+    def step(i, evs=None):
+        if evs:
+            evs[0].record(torch.cuda.current_stream())
+        attn.l2norm_rows(x, out=y, norm=n, num_splits=S, workspace=ws)
+        if evs:
+            evs[1].record(torch.cuda.current_stream())
+
+    warm_up(step, warmup, warm_s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_s = sum(durs) / len(durs) * 1e-3
+    e = x.element_size()
+    alg = l2norm_bytes(w.rows, w.H, e, e)
+    gbs = alg / avg_s / 1e9
+    log("l2norm: %s S=%d, %.4f ms, %.0f GB/s" % (w.name, S, avg_s * 1e3, gbs))
+    del x, y, n, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "splits": S, "ms_per_step": round(avg_s * 1e3, 4), "value": round(gbs, 1),
+            "unit": "GB/s", "algorithmic_bytes": alg,
+            "roofline": {"kernel": "l2norm_onepass_kernel" if S == 1 else "l2norm_partial_kernel + l2norm_scale_kernel",
+                         "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
 def time_plan(w):
     """attn_fwd with its plan against the prefill kernel on the same problem."""
     import torch
@@ -523,6 +572,7 @@ def main():
     step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup, args.warm_seconds)
     d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup, args.warm_seconds)
     plan_res = time_plan(synth.PLAN_SHORT_GQA)
+    l2_res = [time_l2norm(w, args.steps, args.warmup, args.warm_seconds) for w in (synth.L2N_ROWS, synth.L2N_LONG)]
     wb = None if args.backward == "none" else synth.WORKLOADS[args.backward or synth.BWD_PREFILL.name]
     if wb is not None:
         b_step_s, b_kern_s, b_flops = time_backward(wb, args.steps, args.warmup, args.warm_seconds)
@@ -561,6 +611,7 @@ def main():
                                 "traffic": measured_traffic("decode_bf16_kernel", wd.name, DECODE_SOURCES)}},
     }
     result["plan"] = plan_res
+    result["l2norm"] = l2_res
     if wb is not None:
         b_kern_tflops = b_flops / b_kern_s / 1e12
         result["backward"] = {

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
     attn_fwd(q, k, v, ...)                     -> (o, lse)   (planned: prefill or split-K)
     attn_fwd_choose_plan(q, k, v, ...)         -> AttnFwdPlan
     attn_bwd(q, k, v, o, lse, dout, ...)       -> (dq, dk, dv)
+    l2norm_rows(x, ...)                        -> (y, norm)  (include/l2norm.h)
 and the conveniences ``prefill`` (= attn_fwd_prefill) and ``decode`` (split-K
 local step followed by the combine on the same stream).
 """
@@ -29,7 +30,8 @@ __all__ = [
     "attn_splitk_combine", "attn_decode_choose_splits", "attn_decode_partial_bytes",
     "attn_device_cu_count", "prefill", "decode", "chunk_length", "AttnFwdArgs", "AttnBwdArgs", "attn_bwd",
     "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_choose_plan", "AttnFwdPlan", "ATTN_PLAN_PREFILL",
-    "ATTN_PLAN_SPLITK",
+    "ATTN_PLAN_SPLITK", "L2NormArgs", "l2norm_rows", "l2norm_choose_splits", "l2norm_workspace_bytes",
+    "l2norm_max_onepass",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +79,17 @@ class AttnBwdArgs(ctypes.Structure):
         ("dk", ctypes.c_void_p), ("dk_strides", _I64x3),
         ("dv", ctypes.c_void_p), ("dv_strides", _I64x3),
         ("workspace", ctypes.c_void_p),
+    ]
+
+
+class L2NormArgs(ctypes.Structure):
+    """Mirror of ``l2norm_args`` in include/l2norm.h."""
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("x_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("x_stride", ctypes.c_int64),
+        ("y", ctypes.c_void_p), ("y_stride", ctypes.c_int64),
+        ("norm", ctypes.c_void_p),
     ]
 
 
@@ -137,6 +150,21 @@ def load_library():
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_args_size.argtypes = []
     lib.attn_bwd_args_size.restype = ctypes.c_size_t
+    PL = ctypes.POINTER(L2NormArgs)
+    lib.l2norm_rows.argtypes = [PL, i32, vp, ctypes.c_size_t, vp]
+    lib.l2norm_rows.restype = ctypes.c_int
+    lib.l2norm_validate.argtypes = [PL, i32]
+    lib.l2norm_validate.restype = ctypes.c_int
+    lib.l2norm_choose_splits.argtypes = [i64, i64, i32, i32]
+    lib.l2norm_choose_splits.restype = i32
+    lib.l2norm_max_onepass.argtypes = [i32]
+    lib.l2norm_max_onepass.restype = i64
+    lib.l2norm_workspace_bytes.argtypes = [i64, i32]
+    lib.l2norm_workspace_bytes.restype = ctypes.c_size_t
+    lib.l2norm_args_size.argtypes = []
+    lib.l2norm_args_size.restype = ctypes.c_size_t
+    if lib.l2norm_args_size() != ctypes.sizeof(L2NormArgs):
+        raise ImportError("l2norm_args layout mismatch between include/l2norm.h and the binding")
     if lib.attn_fwd_args_size() != ctypes.sizeof(AttnFwdArgs):
         raise ImportError("attn_fwd_args layout mismatch between include/attn.h and the binding")
     if lib.attn_bwd_args_size() != ctypes.sizeof(AttnBwdArgs):
@@ -458,3 +486,49 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bi
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
     return out, lse
+
+
+def l2norm_max_onepass(dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load_library().l2norm_max_onepass(_dtype_code(dtype)))
+
+
+def l2norm_choose_splits(rows: int, H: int, dtype: torch.dtype = torch.bfloat16, cu_count: int = 0) -> int:
+    return int(load_library().l2norm_choose_splits(rows, H, _dtype_code(dtype), cu_count))
+
+
+def l2norm_workspace_bytes(rows: int, num_splits: int) -> int:
+    return int(load_library().l2norm_workspace_bytes(rows, num_splits))
+
+
+def l2norm_rows(x, *, out=None, out_dtype: Optional[torch.dtype] = None, norm=None, return_y: bool = True,
+                num_splits: Optional[int] = None, workspace=None):
+    """Row L2 norm of a 2-D GPU tensor x [rows, H] (bf16 or fp32, unit stride
+    along H): returns (y = x / norm or None, norm [rows] fp32).  num_splits
+    None picks one pass or split-K (l2norm_choose_splits)."""
+    lib = load_library()
+    if x.dim() != 2 or not x.is_cuda or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be a 2-D GPU tensor with unit stride along rows")
+    rows, H = x.shape
+    if num_splits is None:
+        num_splits = l2norm_choose_splits(rows, H, x.dtype, attn_device_cu_count(x.device.index or 0))
+    if out is None and return_y:
+        out = torch.empty((rows, H), dtype=out_dtype or x.dtype, device=x.device)
+    if norm is None:
+        norm = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    need = l2norm_workspace_bytes(rows, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    a = L2NormArgs()
+    a.rows, a.H = rows, H
+    a.x_dtype = _dtype_code(x.dtype)
+    a.x, a.x_stride = x.data_ptr(), int(x.stride(0)) if rows > 0 else H
+    if out is not None:
+        if out.shape != x.shape or (H > 1 and out.stride(1) != 1):
+            raise ValueError("out must be [rows, H] with unit stride along rows")
+        a.y, a.y_stride, a.y_dtype = out.data_ptr(), int(out.stride(0)) if rows > 0 else H, _dtype_code(out.dtype)
+    a.norm = norm.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.l2norm_rows(ctypes.byref(a), int(num_splits), _ptr(workspace), ws_bytes, _stream(x.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "l2norm_rows")
+    return out, norm

@@ -107,6 +107,20 @@ struct CombineParams {
     int o_bf16;
 };
 
+// Row-wise L2 norm (one pass when S <= 1, else split over the row).  Strides
+// in elements; ws holds rows * S (int exponent, float scaled sum) pairs.
+struct L2Params {
+    const void *x;
+    int64_t x_stride;
+    void *y;
+    int64_t y_stride;
+    float *norm;
+    int64_t rows, H;
+    int x_bf16, y_bf16;
+    int S, chunk_vecs;                  // split count, 16-byte vectors per chunk
+    void *ws;
+};
+
 // bf16 prefill with the rolling update (matrix cores, D in {64, 128}).
 hipError_t launch_prefill_bf16(const FwdParams &p, hipStream_t stream);
 // bf16 split-K decode partials (matrix cores, D in {64, 128}).
@@ -115,6 +129,8 @@ hipError_t launch_decode_bf16(const FwdParams &p, hipStream_t stream);
 hipError_t launch_rows_f32(const FwdParams &p, int partial, hipStream_t stream);
 // log-sum-exp combine of split-K partials.
 hipError_t launch_combine(const CombineParams &c, hipStream_t stream);
+// row-wise L2 norm
+hipError_t launch_l2norm(const L2Params &p, hipStream_t stream);
 // bf16 backward: dQ (and Delta, LSE in log2 units), then dK and dV.
 hipError_t launch_bwd_bf16(const BwdParams &p, hipStream_t stream);
 

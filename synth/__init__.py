@@ -98,6 +98,35 @@ WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PRE
                                  SOFTCAP_PREFILL, WINDOW_PREFILL, BWD_PREFILL, PLAN_SHORT_GQA)}
 
 
+@dataclass(frozen=True)
+class RowsWorkload:
+    """Rows of a matrix for the row L2 norm: x ~ N(0, 1) scaled per row."""
+    name: str
+    rows: int
+    H: int
+    dtype: str
+    seed: int
+
+
+# The row L2 norm (the Neptune notes, sections 4 and 9, list the numerically
+# stable L2 norm among the reductions of the same repair algebra): a batch of
+# 32768 rows of 4096 bf16 values (one pass, rows in registers), and 8 rows of
+# 4194304 fp32 values (split over the row).  Rows are N(0, 1) times 2^k with k
+# cycling over -60 .. 60 in steps of 20, so magnitudes span far beyond what a
+# plain fp32 sum of squares holds.
+L2N_ROWS = RowsWorkload("l2norm-bf16-rows32768-H4096", 32768, 4096, "bf16", 1010)
+L2N_LONG = RowsWorkload("l2norm-f32-rows8-H4194304", 8, 4194304, "f32", 1011)
+ROW_WORKLOADS = {w.name: w for w in (L2N_ROWS, L2N_LONG)}
+
+
+def make_rows(w: RowsWorkload, device="cpu") -> torch.Tensor:
+    """x [rows, H] in the workload's dtype: N(0, 1) times 2^(20 * (r % 7) - 60) for row r."""
+    x = torch.randn((w.rows, w.H), generator=_gen(w.seed, TENSOR_Q, device), device=device, dtype=torch.float32)
+    k = (torch.arange(w.rows, device=device) % 7) * 20 - 60
+    x *= torch.pow(2.0, k.to(torch.float32))[:, None]
+    return x.to(torch_dtype(w.dtype))
+
+
 def torch_dtype(name: str) -> torch.dtype:
     return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
 

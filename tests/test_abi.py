@@ -10,7 +10,8 @@ import pytest
 import online_softmax_fusion_amd as attn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, INVALID, UNSUPPORTED = attn.ATTN_OK, attn.ATTN_ERR_INVALID_ARG, attn.ATTN_ERR_UNSUPPORTED
 
@@ -19,9 +20,11 @@ P1, P2, P3, P4, P5, P6 = (0x10000 * (i + 1) for i in range(6))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:attn|l2norm)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd_prefill", "attn_fwd_decode_splitk", "attn_splitk_combine", "attn_bwd"):
+    for n in ("attn_fwd_prefill", "attn_fwd_decode_splitk", "attn_splitk_combine", "attn_bwd", "attn_fwd",
+              "l2norm_rows"):
         assert n in names
 
 
@@ -229,3 +233,63 @@ def test_bwd_workspace_bytes(lib):
     assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 2 * 32 * 4
     assert lib.attn_bwd_workspace_bytes(1, 1, 4) == 32
     assert lib.attn_bwd_workspace_bytes(0, 8, 8) == 0
+
+
+# ----------------------------------------------------------------------------
+# row L2 norm
+# ----------------------------------------------------------------------------
+def good_l2(H=4096, dtype=attn.ATTN_BF16):
+    a = attn.L2NormArgs()
+    a.rows, a.H = 10, H
+    a.x_dtype = a.y_dtype = dtype
+    a.x, a.x_stride = P1, H
+    a.y, a.y_stride = P2, H
+    a.norm = P3
+    return a
+
+
+def test_l2norm_struct_and_limits(lib):
+    assert lib.l2norm_args_size() == ctypes.sizeof(attn.L2NormArgs) == 64
+    assert lib.l2norm_max_onepass(attn.ATTN_BF16) == 8192
+    assert lib.l2norm_max_onepass(attn.ATTN_F32) == 4096
+    assert lib.l2norm_validate(ctypes.byref(good_l2()), 1) == OK
+    assert lib.l2norm_validate(ctypes.byref(good_l2(100000)), 7) == OK
+
+
+@pytest.mark.parametrize("mutate,splits,expect", [
+    (lambda a: setattr(a, "rows", -1), 1, INVALID),
+    (lambda a: setattr(a, "x_dtype", 5), 1, INVALID),
+    (lambda a: setattr(a, "x", None), 1, INVALID),
+    (lambda a: setattr(a, "x_stride", 100), 1, INVALID),        # shorter than a row
+    (lambda a: (setattr(a, "y", None), setattr(a, "norm", None)), 1, INVALID),   # nothing to write
+    (lambda a: setattr(a, "norm", P3 + 2), 1, INVALID),
+    (lambda a: None, 0, INVALID),
+    (lambda a: setattr(a, "H", 4100), 1, UNSUPPORTED),          # not a multiple of 8 bf16
+    (lambda a: setattr(a, "x", P1 + 8), 1, UNSUPPORTED),
+    (lambda a: setattr(a, "y_stride", 4100), 1, UNSUPPORTED),
+    (lambda a: setattr(a, "H", 8200), 1, UNSUPPORTED),          # too long for one pass
+])
+def test_l2norm_rejects(lib, mutate, splits, expect):
+    a = good_l2()
+    a.x_stride = a.y_stride = 8200
+    mutate(a)
+    assert lib.l2norm_validate(ctypes.byref(a), splits) == expect
+    assert lib.l2norm_rows(ctypes.byref(a), splits, None, 0, None) == expect
+
+
+def test_l2norm_split_workspace_checked_first(lib):
+    a = good_l2(100000)
+    a.x_stride = a.y_stride = 100000
+    assert lib.l2norm_workspace_bytes(10, 7) == 10 * 7 * 8
+    assert lib.l2norm_rows(ctypes.byref(a), 7, None, 0, None) == attn.ATTN_ERR_WORKSPACE
+    assert lib.l2norm_rows(ctypes.byref(a), 7, P4, 10 * 7 * 8 - 1, None) == attn.ATTN_ERR_WORKSPACE
+
+
+def test_l2norm_choose_splits(lib):
+    f = lib.l2norm_choose_splits
+    assert f(32768, 4096, attn.ATTN_BF16, 256) == 1          # fits one pass
+    assert f(8, 8192, attn.ATTN_BF16, 256) == 1
+    assert f(8, 8200, attn.ATTN_BF16, 256) == 4               # 16400 bytes: at least 4096 per chunk
+    assert f(8, 4194304, attn.ATTN_F32, 256) == 128           # four workgroups per CU
+    assert f(10000, 1 << 20, attn.ATTN_BF16, 256) == 2        # enough rows already: the minimum split
+    assert f(0, 1 << 20, attn.ATTN_BF16, 256) == 1

@@ -89,3 +89,9 @@ def test_backward_flops_are_five_products():
         b = bench.backward_flops(2, 3, 40, 50, 64, causal, window)
         assert 2 * b == 5 * f
     assert bench.backward_flops(4, 32, 4096, 4096, 128, False) == 10 * 128 * 4 * 32 * 4096 * 4096
+
+
+def test_l2norm_bytes():
+    # x read once, y written once, a 4-byte norm per row
+    assert bench.l2norm_bytes(32768, 4096, 2, 2) == 32768 * 4096 * 4 + 32768 * 4
+    assert bench.l2norm_bytes(8, 4194304, 4, 4) == 8 * 4194304 * 8 + 32

@@ -55,7 +55,7 @@ def test_m0_only_in_inline_asm(src, tmp_path):
 
 
 @needs_hipcc
-@pytest.mark.parametrize("src", ["decode_bf16.hip", "prefill_bf16.hip", "bwd_bf16.hip"])
+@pytest.mark.parametrize("src", ["decode_bf16.hip", "prefill_bf16.hip", "bwd_bf16.hip", "l2norm.hip"])
 def test_no_scratch(src, tmp_path):
     asm = device_asm(src, tmp_path)
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", asm)]

@@ -128,3 +128,25 @@ def test_backward_fullsize_sampled_heads(w):
         print("%s %s: max|err|/max|ref| <= %.2e" % (w.name, name, max(
             float(np.max(np.abs(g[n] - ref[n]))) / float(np.max(np.abs(ref[n]))) for n in range(len(heads)))),
             flush=True)
+
+
+@pytest.mark.parametrize("w", [synth.L2N_ROWS, synth.L2N_LONG], ids=lambda w: w.name)
+def test_l2norm_fullsize(w):
+    """The row L2 norm workloads in the configuration bench.py times (split
+    count from l2norm_choose_splits), norms of every row and sampled rows of
+    y against the oracle, under the tolerances of tests/test_l2norm_gpu.py."""
+    print("full-size l2norm", w.name, flush=True)
+    x = synth.make_rows(w, device="cuda")
+    S = attn.l2norm_choose_splits(w.rows, w.H, x.dtype, attn.attn_device_cu_count(0))
+    y, n = attn.l2norm_rows(x, num_splits=S)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    rows = sorted(set([0, 1, w.rows - 1] + rng.integers(0, w.rows, size=min(w.rows, 64)).tolist()))
+    xs = x[rows].float().cpu()
+    Y, N = oracle.l2norm(xs)
+    ng = n[rows].double().cpu().numpy()
+    assert float(np.max(np.abs(ng - N) / N)) <= 1e-5
+    yg = y[rows].float().cpu().double().numpy()
+    tol = 2.0 ** -8 + 1e-5 if x.dtype == torch.bfloat16 else 1e-5 + 2.0 ** -24
+    assert np.all(np.abs(yg - Y) <= tol * np.abs(Y) + 1e-37)
+    print("%s: S=%d, worst norm rel err %.2e" % (w.name, S, float(np.max(np.abs(ng - N) / N))), flush=True)
