@@ -127,6 +127,8 @@ def source_digest(paths) -> str:
 
 PREFILL_SOURCES = ["online_softmax_fusion_amd/csrc/prefill_bf16.hip", "online_softmax_fusion_amd/csrc/attn_device.h"]
 DECODE_SOURCES = ["online_softmax_fusion_amd/csrc/decode_bf16.hip", "online_softmax_fusion_amd/csrc/attn_device.h"]
+BWD_SOURCES = ["online_softmax_fusion_amd/csrc/bwd_bf16.hip", "online_softmax_fusion_amd/csrc/attn_device.h"]
+L2NORM_SOURCES = ["online_softmax_fusion_amd/csrc/l2norm.hip", "online_softmax_fusion_amd/csrc/attn_device.h"]
 
 
 def measured_traffic(kernel: str, workload: str, sources) -> "int | None":
@@ -142,6 +144,17 @@ def measured_traffic(kernel: str, workload: str, sources) -> "int | None":
     if not ent or ent.get("workload") != workload or ent.get("source_digest") != source_digest(sources):
         return None
     return int(ent["traffic_bytes"])
+
+
+def _sum_traffic(parts):
+    """Total measured bytes per step of several kernels, or None if any is missing or stale."""
+    total = 0
+    for kernel, workload, sources in parts:
+        t = measured_traffic(kernel, workload, sources)
+        if t is None:
+            return None
+        total += t
+    return total
 
 
 # ----------------------------------------------------------------------------
@@ -349,7 +362,10 @@ def time_l2norm(w, steps, warmup, warm_s=1.0):
             "unit": "GB/s", "algorithmic_bytes": alg,
             "roofline": {"kernel": "l2norm_onepass_kernel" if S == 1 else "l2norm_partial_kernel + l2norm_scale_kernel",
                          "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": _sum_traffic([("l2norm_onepass_kernel", w.name, L2NORM_SOURCES)] if S == 1 else
+                                                 [("l2norm_partial_kernel", w.name, L2NORM_SOURCES),
+                                                  ("l2norm_scale_kernel", w.name, L2NORM_SOURCES)])}}
 
 
 def time_plan(w):
@@ -454,15 +470,18 @@ def cpu_baseline(w, budget_s=15.0):
                       (n, G, w.Lq, w.Lk, ", causal" if w.causal else "", w.D, w.name, t1)}
 
 
-def _counter_kib(csv_path, counter, kernel_substr):
+def _counter_kib(csv_path, counter, kernel_substr, grid=None):
     """Mean value of `counter` (KiB) over the dispatches whose kernel name
-    contains `kernel_substr` in a rocprofv3 counter_collection.csv."""
+    contains `kernel_substr` (and, if given, whose grid has `grid` work-items:
+    the bench launches some kernels on more than one shape) in a rocprofv3
+    counter_collection.csv."""
     import csv
 
     vals = []
     with open(csv_path) as f:
         for row in csv.DictReader(f):
-            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"] and \
+                    (grid is None or int(row["Grid_Size"]) == grid):
                 vals.append(float(row["Counter_Value"]))
     if not vals:
         raise ValueError("no %s samples for %s in %s" % (counter, kernel_substr, csv_path))
@@ -493,20 +512,41 @@ def traffic_table(d):
                      "bench.py reports null traffic once that source changes.",
            "calibration": {"copy_bytes": copy_bytes, "fetch_kib_per_copy": cf, "write_kib_per_copy": cw,
                            "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5)}}
-    wp, wd = synth.C2_CAUSAL, synth.C4_DECODE
+    wp, wd, wbk, wl, wll = synth.C2_CAUSAL, synth.C4_DECODE, synth.BWD_PREFILL, synth.L2N_ROWS, synth.L2N_LONG
     S = wd.splits
-    entries = [("prefill_bf16_kernel", wp, PREFILL_SOURCES,
-                prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.Lq, wp.Lk, wp.D)),
-               ("decode_bf16_kernel", wd, DECODE_SOURCES,
-                decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S))]
-    for kernel, w, srcs, alg in entries:
-        fk = _counter_kib(csv_of("fetch"), "FETCH_SIZE", kernel)
-        wk = _counter_kib(csv_of("write"), "WRITE_SIZE", kernel)
-        fb, wb = int(round(fk * 1024 * fscale)), int(round(wk * 1024 * wscale))
-        out[kernel] = {"workload": w.name, "source_digest": source_digest(srcs),
+    Sl = 128                                        # l2norm_choose_splits for the long rows on 256 CUs
+    q_e = wbk.B * wbk.Hq * wbk.Lq * wbk.D * 2           # one [B, Hq, L, D] bf16 tensor
+    kv_e = wbk.B * wbk.Hkv * wbk.Lk * wbk.D * 2
+    rows4 = wbk.B * wbk.Hq * wbk.Lq * 4                # one fp32 value per query row
+    entries = [
+        # kernel, workload, sources, algorithmic bytes, grid work-items of that workload's launch
+        ("prefill_bf16_kernel", wp, PREFILL_SOURCES, prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.Lq, wp.Lk, wp.D),
+         (wp.Lq // 128) * wp.B * wp.Hq * 256),
+        ("decode_bf16_kernel", wd, DECODE_SOURCES,
+         decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S), S * wd.B * wd.Hkv * 256),
+        # dQ: reads Q, dO, O, LSE, K, V; writes dQ, Delta, LSE*log2(e)
+        ("bwd_dq_kernel", wbk, BWD_SOURCES, 4 * q_e + rows4 + 2 * kv_e + 2 * rows4,
+         (wbk.Lq // 128) * wbk.B * wbk.Hq * 256),
+        # dK/dV: reads Q, dO, Delta, LSE*log2(e), K, V; writes dK, dV
+        ("bwd_dkdv_kernel", wbk, BWD_SOURCES, 2 * q_e + 2 * rows4 + 4 * kv_e, (wbk.Lk // 128) * wbk.B * wbk.Hkv * 256),
+        ("l2norm_onepass_kernel", wl, L2NORM_SOURCES, l2norm_bytes(wl.rows, wl.H, 2, 2), (wl.rows // 4) * 256),
+        # split path: the partial kernel reads x and writes one partial per chunk; the scale kernel
+        # reads the partials and x and writes y and the norms
+        ("l2norm_partial_kernel", wll, L2NORM_SOURCES, wll.rows * wll.H * 4 + wll.rows * Sl * 8, wll.rows * Sl * 256),
+        ("l2norm_scale_kernel", wll, L2NORM_SOURCES, wll.rows * wll.H * 8 + wll.rows * Sl * 8 + wll.rows * 4,
+         wll.rows * Sl * 256),
+    ]
+    for kernel, w, srcs, alg, grid in entries:
+        try:
+            fk = _counter_kib(csv_of("fetch"), "FETCH_SIZE", kernel, grid)
+            wk = _counter_kib(csv_of("write"), "WRITE_SIZE", kernel, grid)
+        except ValueError:
+            continue
+        fb, wbytes = int(round(fk * 1024 * fscale)), int(round(wk * 1024 * wscale))
+        out[kernel] = {"workload": w.name, "grid_work_items": grid, "source_digest": source_digest(srcs),
                        "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
-                       "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
-                       "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 4)}
+                       "fetch_bytes": fb, "write_bytes": wbytes, "traffic_bytes": fb + wbytes,
+                       "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wbytes) / alg, 4)}
     return out
 
 
@@ -619,7 +659,9 @@ def main():
             "unit": "TFLOP/s", "ms_per_step": round(b_step_s * 1e3, 4),
             "roofline": {"kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
                          "achieved": round(b_kern_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(b_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "frac": round(b_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": _sum_traffic([("bwd_dq_kernel", wb.name, BWD_SOURCES),
+                                                  ("bwd_dkdv_kernel", wb.name, BWD_SOURCES)])}}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wp, args.cpu_budget)
     else:
