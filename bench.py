@@ -520,7 +520,9 @@ def traffic_table(d):
     rows4 = wbk.B * wbk.Hq * wbk.Lq * 4                # one fp32 value per query row
     entries = [
         # kernel, workload, sources, algorithmic bytes, grid work-items of that workload's launch
-        ("prefill_bf16_kernel", wp, PREFILL_SOURCES, prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.Lq, wp.Lk, wp.D),
+        # (the prefill entry names its 4-wave form: the backward leg's non-causal forward runs the
+        # 8-wave form on the same grid)
+        ("prefill_bf16_kernel<128, 4,", wp, PREFILL_SOURCES, prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.Lq, wp.Lk, wp.D),
          (wp.Lq // 128) * wp.B * wp.Hq * 256),
         ("decode_bf16_kernel", wd, DECODE_SOURCES,
          decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S), S * wd.B * wd.Hkv * 256),
@@ -536,10 +538,11 @@ def traffic_table(d):
         ("l2norm_scale_kernel", wll, L2NORM_SOURCES, wll.rows * wll.H * 8 + wll.rows * Sl * 8 + wll.rows * 4,
          wll.rows * Sl * 256),
     ]
-    for kernel, w, srcs, alg, grid in entries:
+    for match, w, srcs, alg, grid in entries:
+        kernel = match.split("<")[0]
         try:
-            fk = _counter_kib(csv_of("fetch"), "FETCH_SIZE", kernel, grid)
-            wk = _counter_kib(csv_of("write"), "WRITE_SIZE", kernel, grid)
+            fk = _counter_kib(csv_of("fetch"), "FETCH_SIZE", match, grid)
+            wk = _counter_kib(csv_of("write"), "WRITE_SIZE", match, grid)
         except ValueError:
             continue
         fb, wbytes = int(round(fk * 1024 * fscale)), int(round(wk * 1024 * wscale))

@@ -1,7 +1,8 @@
 // prefill_bf16.hip -- fused attention forward for bf16 Q/K/V on gfx950.
 //
-// One workgroup owns a tile of BR = 32 * NW query rows of one (b, h) and
-// rolls over the keys in tiles of BC = 64 (the rolling update of
+// One workgroup owns a tile of BR = 32 * NW query rows of one (b, h) (NW = 4
+// or 8 waves, chosen per problem, see prefill_waves) and rolls over the keys
+// in tiles of BC = 64 (the rolling update of
 // "Neptune论文浅读" section 5; the same three-level loop as the kernel in the
 // CANN FlashAttention post: query tile outside, K/V tiles inside, on-chip
 // compute innermost).  Per K/V tile and per wave (32 query rows):
@@ -239,7 +240,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, co
     } while (0)
 
 template <int D, int NW, int BIAS, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(FwdParams p) {
     using C = TileCfg<D>;
     constexpr int BR = 32 * NW;          // query rows per workgroup
     constexpr int BC = C::BC;
@@ -445,23 +446,49 @@ hipError_t launch_prefill_t(const FwdParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
-    constexpr int NW = 4;
-    // the folded-scale path needs a positive scale; otherwise form the score explicitly
-    const int kind = (p.bias_kind == kBiasNone && !(p.scale_log2 > 0.f)) ? kBiasNoneScaled : p.bias_kind;
+// Waves per workgroup.  Eight waves (256 query rows; the two waves of a SIMD
+// then come from one workgroup) halve the K/V loads per row and the number of
+// workgroups, which pays when each row sees many keys; four waves (128 rows;
+// the two waves of a SIMD come from two independent workgroups) overlap the
+// vector-heavy phases of the two waves better and leave twice as many
+// workgroups for short or unbalanced (causal) rows.  Measured on MI355X
+// (d = 128): eight waves are 1-6% faster for rows that see 4096 or more keys
+// on average (causal 8192, 16384, 32768; non-causal 4096, 8192; ALiBi
+// causal 8192), and 4-19% slower below that (causal 2048, 4096), with the
+// soft cap (15%), and for a 4096-key sliding window (1%); with only 16 query
+// rows against 32768 keys they are 38% slower (seven of the eight waves idle).
+int prefill_waves(const FwdParams &p) {
+    if (p.D != 128 || bias_cap(p.bias_kind) || p.window) return 4;   // the rule was measured at d = 128
+    if (p.Lq < 1024) return 4;   // few rows: most waves of a 256-row tile would idle (Lq = 16: 678 vs 490 us)
+    const int64_t avg_keys = p.causal ? (int64_t)p.Lk - ((int64_t)p.Lq - 1) / 2 : (int64_t)p.Lk;
+    return avg_keys >= 4096 ? 8 : 4;
+}
+
+template <int D, int NW>
+hipError_t launch_prefill_k(const FwdParams &p, int kind, hipStream_t stream) {
     switch (kind) {
         case kBiasNone: return launch_prefill_t<D, NW, kBiasNone>(p, stream);
         case kBiasNoneScaled: return launch_prefill_t<D, NW, kBiasNoneScaled>(p, stream);
         case kBiasAlibi: return launch_prefill_t<D, NW, kBiasAlibi>(p, stream);
         case kBiasDenseF32: return launch_prefill_t<D, NW, kBiasDenseF32>(p, stream);
         case kBiasDenseBf16: return launch_prefill_t<D, NW, kBiasDenseBf16>(p, stream);
-        case kBiasNoneCap: return launch_prefill_t<D, NW, kBiasNoneCap>(p, stream);
-        case kBiasAlibiCap: return launch_prefill_t<D, NW, kBiasAlibiCap>(p, stream);
-        case kBiasDenseF32Cap: return launch_prefill_t<D, NW, kBiasDenseF32Cap>(p, stream);
-        case kBiasDenseBf16Cap: return launch_prefill_t<D, NW, kBiasDenseBf16Cap>(p, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int D>
+hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
+    // the folded-scale path needs a positive scale; otherwise form the score explicitly
+    const int kind = (p.bias_kind == kBiasNone && !(p.scale_log2 > 0.f)) ? kBiasNoneScaled : p.bias_kind;
+    switch (kind) {   // the soft-capped kinds run with four waves only
+        case kBiasNoneCap: return launch_prefill_t<D, 4, kBiasNoneCap>(p, stream);
+        case kBiasAlibiCap: return launch_prefill_t<D, 4, kBiasAlibiCap>(p, stream);
+        case kBiasDenseF32Cap: return launch_prefill_t<D, 4, kBiasDenseF32Cap>(p, stream);
+        case kBiasDenseBf16Cap: return launch_prefill_t<D, 4, kBiasDenseBf16Cap>(p, stream);
+        default: break;
+    }
+    if (D == 128 && prefill_waves(p) == 8) return launch_prefill_k<D, 8>(p, kind, stream);
+    return launch_prefill_k<D, 4>(p, kind, stream);
 }
 
 }  // namespace

@@ -76,6 +76,10 @@ PREFILL_CASES = [
     (2, 2, 2, 130, 190, 128, "bf16", False, "alibi"),
     (2, 2, 2, 96, 140, 128, "bf16", False, "dense_f32"),
     (1, 2, 2, 129, 129, 64, "bf16", True, "dense_bf16"),
+    # >= 1024 rows that see >= 4096 keys on average: the eight-wave (256-row) workgroup
+    (1, 2, 1, 1100, 4200, 128, "bf16", False, "none"),
+    (1, 2, 2, 1030, 4500, 128, "bf16", False, "alibi"),
+    (1, 1, 1, 1300, 6000, 128, "bf16", True, "dense_f32"),
     (1, 1, 1, 1, 77, 128, "bf16", False, "none"),
     (1, 2, 1, 33, 1, 128, "bf16", True, "none"),
 ]
