@@ -201,6 +201,25 @@ def _check_4d(name: str, t: torch.Tensor):
         raise ValueError("%s must be a GPU tensor" % name)
 
 
+def _on(dev: torch.device, name: str, t: Optional[torch.Tensor]):
+    """Every buffer of one call lives on the device the kernels run on."""
+    if t is not None and (not t.is_cuda or t.device != dev):
+        raise ValueError("%s must be on %s, got %s" % (name, dev, t.device))
+
+
+def _check_out(name: str, t: torch.Tensor, shape, dev: torch.device):
+    _check_4d(name, t)
+    _on(dev, name, t)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_lse(lse: torch.Tensor, n: int, dev: torch.device):
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != n:
+        raise ValueError("lse must be a contiguous fp32 tensor of %d elements" % n)
+    _on(dev, "lse", lse)
+
+
 def _strides3(t: torch.Tensor):
     return _I64x3(*[int(x) for x in t.stride()[:3]])
 
@@ -209,6 +228,7 @@ def _make_args(q, k, v, scale, causal, bias, alibi_slopes, o=None, lse=None, sof
                window=None) -> AttnFwdArgs:
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_4d(name, t)
+        _on(q.device, name, t)
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k and v must share one dtype")
     B, Hq, Lq, D = q.shape
@@ -227,8 +247,7 @@ def _make_args(q, k, v, scale, causal, bias, alibi_slopes, o=None, lse=None, sof
     if bias is not None and alibi_slopes is not None:
         raise ValueError("give either a dense bias or ALiBi slopes, not both")
     if bias is not None:
-        if not bias.is_cuda:
-            raise ValueError("bias must be a GPU tensor")
+        _on(q.device, "bias", bias)
         bb = bias
         while bb.dim() < 4:
             bb = bb.unsqueeze(0)
@@ -238,11 +257,15 @@ def _make_args(q, k, v, scale, causal, bias, alibi_slopes, o=None, lse=None, sof
         a.bias_dtype = _dtype_code(bb.dtype)
         a.bias_strides = _I64x4(*[int(x) for x in bb.stride()])
     elif alibi_slopes is not None:
-        if not alibi_slopes.is_cuda or alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq:
+        _on(q.device, "alibi_slopes", alibi_slopes)
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq:
             raise ValueError("alibi_slopes must be a GPU fp32 tensor with one slope per query head")
+        slopes = alibi_slopes.contiguous()
+        a._keep = (slopes,)   # a contiguous copy must outlive the launch that reads it
         a.bias_kind = ATTN_BIAS_ALIBI
-        a.alibi_slopes = alibi_slopes.contiguous().data_ptr()
+        a.alibi_slopes = slopes.data_ptr()
     if o is not None:
+        _on(q.device, "out", o)
         a.o = _ptr(o)
         a.o_dtype = _dtype_code(o.dtype)
         a.o_strides = _strides3(o)
@@ -273,17 +296,19 @@ def attn_fwd_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: O
     position (negative = unbounded).
     """
     lib = load_library()
+    _check_4d("q", q)
     B, Hq, Lq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, Lq, D), dtype=out_dtype or q.dtype, device=q.device)
     else:
-        _check_4d("out", out)
+        _check_out("out", out, (B, Hq, Lq, D), q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq * Lq):
-        raise ValueError("lse must be a contiguous fp32 tensor of B*Hq*Lq elements")
+    if lse is not None:
+        _check_lse(lse, B * Hq * Lq, q.device)
     a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, out, lse, softcap, window)
-    st = lib.attn_fwd_prefill(ctypes.byref(a), _stream(q.device))
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_prefill(ctypes.byref(a), _stream(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_prefill")
     return out, lse
@@ -303,6 +328,7 @@ def attn_fwd_decode_splitk(q, k, v, num_splits: int, scale: Optional[float] = No
                            softcap: float = 0.0, window: Optional[Tuple[int, int]] = None):
     """Split-K local step: partials (o [B,Hq,Lq,S,D], m [B,Hq,Lq,S], l [B,Hq,Lq,S]) in fp32."""
     lib = load_library()
+    _check_4d("q", q)
     B, Hq, Lq, D = q.shape
     S = int(num_splits)
     dev = q.device
@@ -314,10 +340,13 @@ def attn_fwd_decode_splitk(q, k, v, num_splits: int, scale: Optional[float] = No
         l_part = torch.empty((B, Hq, Lq, S), dtype=torch.float32, device=dev)
     for name, t, n in (("o_part", o_part, B * Hq * Lq * S * D), ("m_part", m_part, B * Hq * Lq * S),
                        ("l_part", l_part, B * Hq * Lq * S)):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n or not t.is_cuda:
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
             raise ValueError("%s must be a contiguous GPU fp32 tensor of %d elements" % (name, n))
+        _on(dev, name, t)
     a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, softcap=softcap, window=window)
-    st = lib.attn_fwd_decode_splitk(ctypes.byref(a), S, _ptr(o_part), _ptr(m_part), _ptr(l_part), _stream(dev))
+    with torch.cuda.device(dev):
+        st = lib.attn_fwd_decode_splitk(ctypes.byref(a), S, _ptr(o_part), _ptr(m_part), _ptr(l_part),
+                                        _stream(dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_decode_splitk")
     return o_part, m_part, l_part
@@ -330,19 +359,24 @@ def attn_splitk_combine(o_part, m_part, l_part, *, out=None, out_dtype=torch.bfl
     if o_part.dim() != 5:
         raise ValueError("o_part must be [B, Hq, Lq, S, D]")
     B, Hq, Lq, S, D = o_part.shape
+    dev = o_part.device
     for name, t in (("o_part", o_part), ("m_part", m_part), ("l_part", l_part)):
         if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("%s must be a contiguous GPU fp32 tensor" % name)
+        _on(dev, name, t)
     if tuple(m_part.shape) != (B, Hq, Lq, S) or tuple(l_part.shape) != (B, Hq, Lq, S):
         raise ValueError("m_part and l_part must be [B, Hq, Lq, S]")
     if out is None:
-        out = torch.empty((B, Hq, Lq, D), dtype=out_dtype, device=o_part.device)
+        out = torch.empty((B, Hq, Lq, D), dtype=out_dtype, device=dev)
     else:
-        _check_4d("out", out)
+        _check_out("out", out, (B, Hq, Lq, D), dev)
     if lse is None and return_lse:
-        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=o_part.device)
-    st = lib.attn_splitk_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), B, Hq, Lq, D, S, _ptr(out),
-                                 _dtype_code(out.dtype), _strides3(out), _ptr(lse), _stream(o_part.device))
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_lse(lse, B * Hq * Lq, dev)
+    with torch.cuda.device(dev):
+        st = lib.attn_splitk_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), B, Hq, Lq, D, S, _ptr(out),
+                                     _dtype_code(out.dtype), _strides3(out), _ptr(lse), _stream(dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_splitk_combine")
     return out, lse
@@ -395,17 +429,16 @@ def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool 
     ``attn_fwd_prefill``.  ``workspace`` may be a GPU byte tensor of at least
     ``attn_bwd_workspace_bytes(B, Hq, Lq)`` bytes to reuse."""
     lib = load_library()
+    _check_4d("q", q)
+    _check_4d("k", k)
     B, Hq, Lq, D = q.shape
     _, Hkv, Lk, _ = k.shape
     dev = q.device
     for name, t in (("o", o), ("dout", dout)):
-        _check_4d(name, t)
-        if tuple(t.shape) != (B, Hq, Lq, D):
-            raise ValueError("%s must be [B, Hq, Lq, D]" % name)
+        _check_out(name, t, (B, Hq, Lq, D), dev)
     if dout.dtype != q.dtype:
         raise TypeError("dout must have the dtype of q")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq * Lq or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous GPU fp32 tensor of B*Hq*Lq elements")
+    _check_lse(lse, B * Hq * Lq, dev)
     gdt = grad_dtype or q.dtype
     if dq is None:
         dq = torch.empty((B, Hq, Lq, D), dtype=gdt, device=dev)
@@ -414,23 +447,26 @@ def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool 
     if dv is None:
         dv = torch.empty((B, Hkv, Lk, D), dtype=gdt, device=dev)
     for name, t, shape in (("dq", dq, (B, Hq, Lq, D)), ("dk", dk, (B, Hkv, Lk, D)), ("dv", dv, (B, Hkv, Lk, D))):
-        _check_4d(name, t)
-        if tuple(t.shape) != shape or t.dtype != gdt:
+        _check_out(name, t, shape, dev)
+        if t.dtype != gdt:
             raise ValueError("%s must be %s of dtype %s" % (name, shape, gdt))
     need = attn_bwd_workspace_bytes(B, Hq, Lq)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
-    elif workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+    elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace must be a GPU tensor of at least %d bytes" % need)
+    _on(dev, "workspace", workspace)
     a = AttnBwdArgs()
-    a.fwd = _make_args(q, k, v, scale, causal, bias, alibi_slopes, o, lse, softcap, window)
+    fa = _make_args(q, k, v, scale, causal, bias, alibi_slopes, o, lse, softcap, window)
+    a.fwd = fa   # copies the fields; fa keeps any temporary they point to alive until the launch
     a.dout, a.dout_strides = _ptr(dout), _strides3(dout)
     a.grad_dtype = _dtype_code(gdt)
     a.dq, a.dq_strides = _ptr(dq), _strides3(dq)
     a.dk, a.dk_strides = _ptr(dk), _strides3(dk)
     a.dv, a.dv_strides = _ptr(dv), _strides3(dv)
     a.workspace = _ptr(workspace)
-    st = lib.attn_bwd(ctypes.byref(a), _stream(dev))
+    with torch.cuda.device(dev):
+        st = lib.attn_bwd(ctypes.byref(a), _stream(dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
@@ -441,7 +477,7 @@ def attn_fwd_choose_plan(q, k, v, scale: Optional[float] = None, causal: bool = 
                          cu_count: int = 0, out_dtype: Optional[torch.dtype] = None) -> AttnFwdPlan:
     """The plan (prefill or split-K with its split count and workspace size)
     attn_fwd would run for these arguments on a device with ``cu_count``
-    compute units (0: the current device's)."""
+    compute units (0: the count of the device q is on)."""
     lib = load_library()
     if cu_count <= 0:
         cu_count = attn_device_cu_count(q.device.index or 0)
@@ -465,15 +501,16 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bi
     ``attn_fwd_prefill``; ``workspace`` may be a GPU byte tensor to reuse (a
     new one of the plan's size is allocated otherwise)."""
     lib = load_library()
+    _check_4d("q", q)
     B, Hq, Lq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, Lq, D), dtype=out_dtype or q.dtype, device=q.device)
     else:
-        _check_4d("out", out)
+        _check_out("out", out, (B, Hq, Lq, D), q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq * Lq):
-        raise ValueError("lse must be a contiguous fp32 tensor of B*Hq*Lq elements")
+    if lse is not None:
+        _check_lse(lse, B * Hq * Lq, q.device)
     a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, out, lse, softcap, window)
     plan = AttnFwdPlan()
     st = lib.attn_fwd_choose_plan(ctypes.byref(a), attn_device_cu_count(q.device.index or 0), ctypes.byref(plan))
@@ -481,8 +518,10 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bi
         raise AttnError(st, "attn_fwd_choose_plan")
     if workspace is None and plan.workspace_bytes > 0:
         workspace = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device=q.device)
+    _on(q.device, "workspace", workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.attn_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(q.device))
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
     return out, lse
@@ -515,9 +554,13 @@ def l2norm_rows(x, *, out=None, out_dtype: Optional[torch.dtype] = None, norm=No
         out = torch.empty((rows, H), dtype=out_dtype or x.dtype, device=x.device)
     if norm is None:
         norm = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    elif norm.dtype != torch.float32 or not norm.is_contiguous() or norm.numel() != rows:
+        raise ValueError("norm must be a contiguous fp32 tensor of %d elements" % rows)
+    _on(x.device, "norm", norm)
     need = l2norm_workspace_bytes(rows, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    _on(x.device, "workspace", workspace)
     a = L2NormArgs()
     a.rows, a.H = rows, H
     a.x_dtype = _dtype_code(x.dtype)
@@ -525,10 +568,12 @@ def l2norm_rows(x, *, out=None, out_dtype: Optional[torch.dtype] = None, norm=No
     if out is not None:
         if out.shape != x.shape or (H > 1 and out.stride(1) != 1):
             raise ValueError("out must be [rows, H] with unit stride along rows")
+        _on(x.device, "out", out)
         a.y, a.y_stride, a.y_dtype = out.data_ptr(), int(out.stride(0)) if rows > 0 else H, _dtype_code(out.dtype)
     a.norm = norm.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.l2norm_rows(ctypes.byref(a), int(num_splits), _ptr(workspace), ws_bytes, _stream(x.device))
+    with torch.cuda.device(x.device):
+        st = lib.l2norm_rows(ctypes.byref(a), int(num_splits), _ptr(workspace), ws_bytes, _stream(x.device))
     if st != ATTN_OK:
         raise AttnError(st, "l2norm_rows")
     return out, norm
