@@ -430,9 +430,11 @@ __device__ __forceinline__ void dkdv_scores(const FwdParams &p, const f32x16 &s,
                                             int imin, int imax, float slope_l2, int b, int h, uint32_t (&pk)[8],
                                             uint32_t (&dk)[8]) {
     const float dbase = (float)(ibase + (p.Lk - p.Lq) - key);
-    // element offset eo is visible iff (unsigned)(eo - lo) <= span
-    const int lo = imin - ibase;
-    const uint32_t span = (uint32_t)(imax - imin);
+    // element offset eo is visible iff (unsigned)(eo - lo) <= span; a key no
+    // row sees (imax < imin) gets lo = -1, span = 0, which admits no eo >= 0
+    const bool seen = imax >= imin;
+    const int lo = seen ? imin - ibase : -1;
+    const uint32_t span = seen ? (uint32_t)(imax - imin) : 0u;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
         float pr[2], du[2];

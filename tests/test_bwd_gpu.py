@@ -52,6 +52,13 @@ def grad_errors(got, ref):
 
 def check_grads(got, refs, what):
     out = []
+    # a key no query row sees (dV_j = sum_i P_ij dO_i is exactly 0 in the
+    # oracle only then) must get exactly 0 in dK and dV
+    dead = np.all(refs[2] == 0.0, axis=-1)
+    if dead.any():
+        for name, g in (("dk", got[1]), ("dv", got[2])):
+            gd = g.float().cpu().numpy()[dead]
+            assert np.all(gd == 0.0), "%s %s: %d keys no row sees are not zero" % (what, name, int(dead.sum()))
     for name, g, r in zip(("dq", "dk", "dv"), got, refs):
         mx, fro = grad_errors(g, r)
         print("%s %s: max|err|/max|ref| %.2e  fro %.2e" % (what, name, mx, fro), flush=True)
@@ -107,6 +114,10 @@ BWD_CASES = [
     (1, 2, 2, 300, 150, 128, True, "none", 0.0, None),          # Lq > Lk: rows without keys
     (1, 1, 1, 1, 77, 128, False, "none", 0.0, None),            # one query row
     (1, 2, 1, 33, 1, 128, True, "none", 0.0, None),             # one key
+    # keys below Lk - Lq - left are seen by no row; the 32-key block of keys
+    # 128-159 holds such keys and seen ones (their dK, dV must be exactly 0)
+    (1, 2, 2, 142, 305, 128, True, "none", 0.0, (7, 9)),
+    (1, 4, 2, 100, 300, 64, False, "dense_f32", 0.0, (5, 20)),
 ]
 
 
