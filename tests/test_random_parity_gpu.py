@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": (1e-5, 1e-5), "bf16": (1.5e-2, 1e-3)}
 N_PREFILL, N_DECODE, N_BWD, N_L2 = 48, 32, 20, 16
+N_LONG_PREFILL, N_LONG_BWD = 8, 6
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -30,17 +31,28 @@ def need_gpu():
     attn.load_library()
 
 
-def draw_attention(seed, decode=False, backward=False):
+def draw_attention(seed, decode=False, backward=False, long=False):
     rng = np.random.default_rng(seed)
     c = {}
     c["B"] = int(rng.integers(1, 3))
     c["Hkv"] = int(rng.integers(1, 3))
     c["Hq"] = c["Hkv"] * int(rng.choice([1, 2, 4]))
     c["D"] = int(rng.choice([64, 128]))
-    c["dtype"] = "bf16" if (backward or rng.random() < 0.8) else "f32"
+    c["dtype"] = "bf16" if (backward or long or rng.random() < 0.8) else "f32"
     if decode:
         c["Lq"] = int(rng.integers(1, 5))
         c["Lk"] = int(rng.integers(1, 3000))
+    elif long and backward:
+        c["B"], c["Hkv"], c["Hq"] = 1, 1, int(rng.choice([1, 2]))
+        c["Lq"] = int(rng.integers(500, 1200))
+        c["Lk"] = int(rng.integers(500, 1200))
+    elif long:
+        # enough rows and keys per row for the 256-row (eight-wave) workgroup
+        c["B"], c["Hkv"] = 1, 1
+        c["Hq"] = int(rng.choice([1, 2]))
+        c["D"] = 128
+        c["Lq"] = int(rng.integers(1024, 1700))
+        c["Lk"] = int(rng.integers(4200, 6500))
     else:
         c["Lq"] = int(rng.integers(1, 300))
         c["Lk"] = int(rng.integers(1, 400)) if rng.random() < 0.8 else max(1, c["Lq"] - int(rng.integers(0, 100)))
@@ -50,6 +62,8 @@ def draw_attention(seed, decode=False, backward=False):
     c["window"] = None
     if rng.random() < 0.3:
         c["window"] = (int(rng.integers(-1, 120)), int(rng.integers(-1, 60)))
+    if long and not backward:   # the eight-wave form takes neither cap nor window
+        c["softcap"], c["window"] = 0.0, None
     c["out"] = "f32" if rng.random() < 0.25 else c["dtype"]
     c["splits"] = int(rng.integers(1, 41))
     c["grad"] = "f32" if rng.random() < 0.5 else "bf16"
@@ -101,6 +115,23 @@ def test_random_prefill(i):
     compare(o2, lse2, O_ref, L_ref, c["dtype"], "attn_fwd " + str(c))
 
 
+@pytest.mark.parametrize("i", range(N_LONG_PREFILL))
+def test_random_long_prefill(i):
+    """Shapes that run the 256-row (eight-wave) workgroup, sampled rows."""
+    c = draw_attention(6500 + i, long=True)
+    print("random long prefill", c, flush=True)
+    w, q, k, v, gkw, okw = make(c)
+    od = torch.float32 if c["out"] == "f32" else None
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), c["causal"], out_dtype=od,
+                                   **gkw)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(c["seed"])
+    n = c["B"] * c["Hq"] * c["Lq"]
+    rows = np.unique(np.concatenate([np.arange(0, 300), np.arange(n - 300, n), rng.integers(0, n, 200)]))
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), c["causal"], rows=rows, **okw)
+    compare(o.reshape(n, -1)[rows], lse.reshape(n)[rows], O_ref, L_ref, c["dtype"], str(c))
+
+
 @pytest.mark.parametrize("i", range(N_DECODE))
 def test_random_decode(i):
     c = draw_attention(7000 + i, decode=True)
@@ -114,11 +145,12 @@ def test_random_decode(i):
     compare(o, lse, O_ref, L_ref, c["dtype"], str(c))
 
 
-@pytest.mark.parametrize("i", range(N_BWD))
+@pytest.mark.parametrize("i", range(N_BWD + N_LONG_BWD))
 def test_random_backward(i):
     """Gradients under the bars of the backward parity tests (max |err| <=
-    2e-2 max |ref|, relative Frobenius error <= 8e-3 per tensor)."""
-    c = draw_attention(8000 + i, backward=True)
+    2e-2 max |ref|, relative Frobenius error <= 8e-3 per tensor); the last
+    cases span many query and key tiles."""
+    c = draw_attention(8000 + i, backward=True, long=i >= N_BWD)
     print("random backward", c, flush=True)
     w, q, k, v, gkw, okw = make(c)
     do = synth.make_dout(w)
