@@ -207,14 +207,18 @@ __device__ __forceinline__ uint32_t tile_goff(int wave, int lane, uint32_t lbyte
 // ---------------------------------------------------------------------------
 // dQ kernel
 // ---------------------------------------------------------------------------
-template <int D, int BIAS, bool MASK>
+// One K/V tile for this wave.  `masked` tiles (the causal diagonal, window
+// edges, key tail) zero the scores of keys a row cannot see; only that
+// elementwise step branches on it, so the matrix chains and the dQ
+// accumulators are the same code and registers on both kinds of tile.
+template <int D, int BIAS>
 __device__ __forceinline__ void dq_tile(const FwdParams &p, const char *lk, const char *lv, int rbase, int tbase,
                                         const u32x4 (&qreg)[D / 16], const u32x4 (&doreg)[D / 16],
                                         f32x16 (&dqacc)[D / 32], float lse, float delta, int kt0, int wrow0,
                                         int wjmin, int wjmax, int qpos, int jmin, int jmax, int qrow,
-                                        float slope_l2, int b, int h, int lane) {
+                                        float slope_l2, int b, int h, int lane, bool masked) {
     using C = BwdCfg<D>;
-    if (MASK && !((wrow0 < p.Lq) && kt0 <= wjmax && kt0 + C::BT - 1 >= wjmin)) return;
+    if (masked && !((wrow0 < p.Lq) && kt0 <= wjmax && kt0 + C::BT - 1 >= wjmin)) return;
     const int hh = lane >> 5;
     // S^T = K Q^T and dP^T = V dO^T, two 32-key blocks each
     f32x16 s[2], dp[2];
@@ -229,26 +233,33 @@ __device__ __forceinline__ void dq_tile(const FwdParams &p, const char *lk, cons
             s[kb] = mfma32(as_bf16x8(load16(lk + ((rbase ^ (ks << 5)) + kb * 32 * C::RB))), as_bf16x8(qreg[ks]), s[kb]);
             dp[kb] = mfma32(as_bf16x8(load16(lv + ((rbase ^ (ks << 5)) + kb * 32 * C::RB))), as_bf16x8(doreg[ks]), dp[kb]);
         }
-    // dU = P (dP - Delta) [* slope], packed to bf16 in the B-operand layout
+    // dU = P (dP - Delta) [* slope] (in place of the scores), then on masked
+    // tiles zeroed outside [jmin, jmax], packed to bf16 in the B-operand layout
     const float dbase = (float)(qpos - kt0 - hh * 8);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int eo = kb * 32 + (e >> 3) * 16 + (e & 7);
+            const int j = kt0 + eo + hh * 8;
+            float pr;
+            s[kb][e] = grad_of_score<BIAS>(p, s[kb][e], dp[kb][e], lse, delta, slope_l2, fabsf(dbase - (float)eo),
+                                           dense_bias<BIAS>(p, b, h, qrow, j), &pr);
+        }
+    if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = kt0 + kb * 32 + (e >> 3) * 16 + (e & 7) + hh * 8;
+                if (j < jmin || j > jmax) s[kb][e] = 0.f;
+            }
+    }
     uint32_t dsk[2][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-            float du[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int eo = kb * 32 + ((e + u) >> 3) * 16 + ((e + u) & 7);
-                const int j = kt0 + eo + hh * 8;
-                float pr;
-                du[u] = grad_of_score<BIAS>(p, s[kb][e + u], dp[kb][e + u], lse, delta, slope_l2,
-                                            fabsf(dbase - (float)eo), dense_bias<BIAS>(p, b, h, qrow, j), &pr);
-                if (MASK && (j < jmin || j > jmax)) du[u] = 0.f;
-            }
-            dsk[kb][e >> 1] = pack_bf16x2(du[0], du[1]);
-        }
-    }
+        for (int e = 0; e < 16; e += 2) dsk[kb][e >> 1] = pack_bf16x2(s[kb][e], s[kb][e + 1]);
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int kk = 0; kk < C::BT / 16; ++kk) {
@@ -396,12 +407,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
         const int st = (t - t_first) & 1;
         if (t + 1 < t_end) issue(t + 1, st ^ 1);
         const char *lk = smem + st * STAGE;
-        if (t < u_first || t >= u_end)
-            dq_tile<D, BIAS, true>(p, lk, lk + C::TILE, rbase, tbase, qreg, doreg, dqacc, lse, delta, t * BC, wrow0,
-                                   wjmin, wjmax, qpos, jmin, jmax, qrow, slope_l2, b, h, lane);
-        else
-            dq_tile<D, BIAS, false>(p, lk, lk + C::TILE, rbase, tbase, qreg, doreg, dqacc, lse, delta, t * BC, wrow0,
-                                    wjmin, wjmax, qpos, jmin, jmax, qrow, slope_l2, b, h, lane);
+        dq_tile<D, BIAS>(p, lk, lk + C::TILE, rbase, tbase, qreg, doreg, dqacc, lse, delta, t * BC, wrow0, wjmin,
+                         wjmax, qpos, jmin, jmax, qrow, slope_l2, b, h, lane, t < u_first || t >= u_end);
         wait_all_loads();
         __syncthreads();
     }

@@ -85,3 +85,20 @@ def test_dkdv_loop_keeps_accumulators_in_place(tmp_path):
                 if mv:
                     assert mv.group(2) in zero, (m.group(1), ln.strip())   # copies a zero
                     zero.add(mv.group(1))
+
+
+@needs_hipcc
+def test_dq_loop_keeps_accumulators_in_place(tmp_path):
+    """The dQ kernel's masked and unmasked tiles share one code path (only the
+    elementwise mask branches), so no block with matrix-core work copies
+    registers around (a separate masked path made the compiler move the 64
+    dQ accumulators after every tile)."""
+    asm = device_asm("bwd_bf16.hip", tmp_path)
+    kernels = list(re.finditer(r"^(_ZN4attn\w*bwd_dq_kernel\w*):", asm, flags=re.M))
+    assert kernels
+    for m in kernels:
+        body = asm[m.end():asm.index("s_endpgm", m.end())]
+        for blk in re.split(r"^\.LBB\d+_\d+:", body, flags=re.M):
+            if "v_mfma" in blk:
+                moves = len(re.findall(r"\bv_mov_b(?:32|64)\b|v_accvgpr_(?:mov|read|write)", blk))
+                assert moves < 8, (m.group(1), moves)
