@@ -79,6 +79,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The same descriptor as four words, for inline assembly.
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// Buffer-to-LDS loads: 16 (or 4) bytes per lane from buffer offset voff + soff
+// into LDS at m0 + 16 * lane (4 * lane).  Inline assembly, so that the
+// compiler's wait insertion does not see them: a kernel that uses them waits
+// for them itself (wait_all_loads, or counted vmcnt waits).  With the
+// compiler's builtin, the compiler drains every load in flight before LDS
+// reads it cannot prove independent of the load's target, which serialises
+// loading and computing.  The assembly writes M0: no compiler-generated
+// instruction of a file that uses these may use M0.
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc),
+                 "s"(soff)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const i32x4 &rsrc, uint32_t m0, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+// every vector memory load of this wave has landed (also a compiler barrier)
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // 4 bf16 values from LDS through the transposing read: within each group of

@@ -143,39 +143,6 @@ __device__ __forceinline__ void store4(void *base, int64_t idx, bool bf16, float
     }
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor words: base address, stride 0, `bytes` readable bytes
-// (loads past the end read 0).
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
-}
-
-// Buffer-to-LDS loads: 16 (or 4) bytes per lane from buffer offset voff + soff
-// into LDS at m0 + 16 * lane (4 * lane).  Inline assembly, so that the
-// compiler's wait insertion does not see them: the kernels wait for them
-// themselves (wait_all_loads) before the barrier that ends each tile.  Given
-// the LDS-DMA loads, the compiler drains every load in flight before LDS reads
-// it cannot prove independent, which serialises loading and computing.  No
-// compiler-generated instruction of this file may use M0.
-__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc),
-                 "s"(soff)
-                 : "memory");
-}
-__device__ __forceinline__ void dma4(const i32x4 &rsrc, uint32_t m0, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
-                 : "memory");
-}
-// every vector memory load of this wave has landed (also a compiler barrier)
-__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// LDS byte address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
-}
-
 // A 64-row tile (rows `src` .. + 63, `lbytes` apart, `nvalid` of them present)
 // into the LDS tile at byte address `lds`: lane fills LDS bytes
 // [i*T*16 + wave*1024 + 16*lane, +16) of round i from byte offset goff of the

@@ -43,39 +43,6 @@ namespace {
 
 constexpr float kTau = 8.0f;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// raw buffer descriptor: base address, stride 0, `bytes` readable bytes
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
-}
-
-// 16 bytes per lane from buffer offset voff into LDS at m0 + 16 * lane.
-// Written as inline assembly so that the compiler's own wait insertion does
-// not see these loads: the kernel counts them itself (wait_vmcnt) and
-// otherwise the compiler drains every load in flight before the first LDS
-// read of each loop trip.
-__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t m0, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
-                 : "memory");
-}
-
-// LDS byte address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char *)p);
-}
-
-// 4 bf16 values from LDS through the transposing read: within each group of
-// 16 lanes, lane i receives element (i % 4) of the 8-byte words addressed by
-// lanes 4j + i/4, j = 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
-
 // wait until at most N vector memory loads are outstanding (a compiler
 // barrier for memory accesses as well)
 template <int N>
@@ -184,8 +151,9 @@ __device__ __forceinline__ void decode_block(const FwdParams &p, const char *lk,
         const bf16x8 bop = as_bf16x8(u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const u32x2 lo = lds_read_tr16(lv + (vbase ^ (db << 6)) + half * 16 * C::RB);
-            const u32x2 hi = lds_read_tr16(lv + (vbase ^ (db << 6)) + (half * 16 + 4) * C::RB);
+            const char *vt = lv + (vbase ^ (db << 6));
+            const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vt + half * 16 * C::RB));
+            const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vt + (half * 16 + 4) * C::RB));
             oacc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bop, oacc[db]);
         }
     }
@@ -202,13 +170,13 @@ __device__ __forceinline__ void issue_block(const FwdParams &p, const uint16_t *
                                             const uint32_t (&voff)[BlockCfg<D>::NL]) {
     using C = BlockCfg<D>;
     const int nvalid = min(C::BK, p.Lk - kb0);
-    const i32x4 rk = make_rsrc(kp + (int64_t)kb0 * p.k_sl, (uint32_t)(nvalid - 1) * kl_bytes + D * 2);
-    const i32x4 rv = make_rsrc(vp + (int64_t)kb0 * p.v_sl, (uint32_t)(nvalid - 1) * vl_bytes + D * 2);
+    const i32x4 rk = rsrc_words(kp + (int64_t)kb0 * p.k_sl, (uint32_t)(nvalid - 1) * kl_bytes + D * 2);
+    const i32x4 rv = rsrc_words(vp + (int64_t)kb0 * p.v_sl, (uint32_t)(nvalid - 1) * vl_bytes + D * 2);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < C::NL; ++i) dma16(rk, dst + i * 1024, koff[i]);
+    for (int i = 0; i < C::NL; ++i) dma16(rk, dst + i * 1024, koff[i], 0u);
 #pragma unroll
-    for (int i = 0; i < C::NL; ++i) dma16(rv, dst + C::TB + i * 1024, voff[i]);
+    for (int i = 0; i < C::NL; ++i) dma16(rv, dst + C::TB + i * 1024, voff[i], 0u);
 }
 
 template <int D, int NW, int NST, int BIAS>
