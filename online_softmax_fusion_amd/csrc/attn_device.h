@@ -134,4 +134,31 @@ __device__ __forceinline__ int perm32(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Work order for a grid of per-head tiles.  The dispatcher hands block b to XCD
+// b % 8; block b takes item (b % 8) * (n / 8) + b / 8 of a head-major list, so
+// each XCD runs a contiguous range of heads and a head's K/V stays in that XCD's
+// L2.  `rank` numbers a head's tiles, 0 first.  With `interleave` (tiles of
+// unequal cost, ranked heaviest first), windows of 4 heads, else 2, run their
+// tiles rank by rank across the window: with one head at a time the last head's
+// heaviest tiles start when the XCD is nearly drained and finish alone.
+// Windows are used only where they tile every XCD's range.
+constexpr int kXcds = 8;
+struct WorkItem {
+    int head;
+    int rank;
+};
+__device__ __forceinline__ WorkItem xcd_work_item(int per_head, bool interleave) {
+    const int n = (int)gridDim.x;
+    if (n % kXcds != 0) return {(int)blockIdx.x / per_head, (int)blockIdx.x % per_head};
+    const int per_xcd = n / kXcds;
+    const int item = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    int win = 1;
+    if (interleave) win = per_xcd % (4 * per_head) == 0 ? 4 : per_xcd % (2 * per_head) == 0 ? 2 : 1;
+    const int span = win * per_head;
+    const int w0 = item / span;
+    const int idx = item - w0 * span;
+    const int rank = idx / win;
+    return {w0 * win + (idx - rank * win), rank};
+}
+
 }  // namespace attn

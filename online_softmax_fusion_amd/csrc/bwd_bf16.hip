@@ -43,7 +43,6 @@
 namespace attn {
 namespace {
 
-constexpr int kXcds = 8;
 
 template <int D>
 struct BwdCfg {
@@ -249,14 +248,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-    // work item: XCD-contiguous ranges of a head-major list, heavy tiles first
+    // work item: XCD-contiguous ranges of heads; under a causal mask the last
+    // query tile sees the most keys and goes first
     const int nqt = (p.Lq + BR - 1) / BR;
-    const int nblocks = (int)gridDim.x;
-    int item = blockIdx.x;
-    if (nblocks % kXcds == 0) item = (blockIdx.x % kXcds) * (nblocks / kXcds) + blockIdx.x / kXcds;
-    const int bh = item / nqt;
-    int qt = item - bh * nqt;
-    if (p.causal) qt = nqt - 1 - qt;
+    const WorkItem wi = xcd_work_item(nqt, p.causal && !p.window);
+    const int bh = wi.head;
+    const int qt = p.causal ? nqt - 1 - wi.rank : wi.rank;
     const int b = bh / p.Hq;
     const int h = bh - b * p.Hq;
     const int hk = h / p.G;
@@ -485,14 +482,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-    // work item: XCD-contiguous ranges of a head-major list; key tiles in
-    // ascending order (under the causal mask the first ones see the most rows)
+    // work item: XCD-contiguous ranges of K/V heads; key tiles in ascending
+    // order (under the causal mask the first ones see the most rows)
     const int nkt = (p.Lk + BK - 1) / BK;
-    const int nblocks = (int)gridDim.x;
-    int item = blockIdx.x;
-    if (nblocks % kXcds == 0) item = (blockIdx.x % kXcds) * (nblocks / kXcds) + blockIdx.x / kXcds;
-    const int bhk = item / nkt;
-    const int kt = item - bhk * nkt;
+    const WorkItem wi = xcd_work_item(nkt, p.causal && !p.window);
+    const int bhk = wi.head;
+    const int kt = wi.rank;
     const int b = bhk / p.Hkv;
     const int hk = bhk - b * p.Hkv;
     const int k0 = kt * BK;

@@ -50,7 +50,6 @@ namespace attn {
 namespace {
 
 constexpr float kTau = 8.0f;
-constexpr int kXcds = 8;
 
 template <int D>
 struct TileCfg {
@@ -258,15 +257,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(FwdParams
     __shared__ __attribute__((aligned(1024))) char lds_v0[C::TILE];
     __shared__ __attribute__((aligned(1024))) char lds_v1[C::TILE];
 
-    // work item: XCD-contiguous ranges of a head-major list, heavy tiles first
-    const int BH = p.B * p.Hq;
+    // work item: XCD-contiguous ranges of heads; under a causal mask the last
+    // query tile sees the most keys and goes first
     const int nqt = (p.Lq + BR - 1) / BR;
-    const int nblocks = (int)gridDim.x;
-    int item = blockIdx.x;
-    if (nblocks % kXcds == 0) item = (blockIdx.x % kXcds) * (nblocks / kXcds) + blockIdx.x / kXcds;
-    const int bh = item / nqt;
-    int qt = item - bh * nqt;
-    if (p.causal) qt = nqt - 1 - qt;
+    const WorkItem wi = xcd_work_item(nqt, p.causal && !p.window);
+    const int bh = wi.head;
+    const int qt = p.causal ? nqt - 1 - wi.rank : wi.rank;
     const int b = bh / p.Hq;
     const int h = bh - b * p.Hq;
     const int hk = h / p.G;

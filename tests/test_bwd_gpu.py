@@ -118,6 +118,10 @@ BWD_CASES = [
     # 128-159 holds such keys and seen ones (their dK, dV must be exactly 0)
     (1, 2, 2, 142, 305, 128, True, "none", 0.0, (7, 9)),
     (1, 4, 2, 100, 300, 64, False, "dense_f32", 0.0, (5, 20)),
+    # causal work order: 2 query tiles and 2 key tiles per head; 32 heads run in
+    # windows of 4 heads, 16 K/V heads (dK/dV) in windows of 2
+    (2, 16, 16, 200, 200, 128, True, "none", 0.0, None),
+    (1, 32, 16, 256, 256, 64, True, "none", 0.0, None),
 ]
 
 

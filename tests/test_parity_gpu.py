@@ -82,6 +82,12 @@ PREFILL_CASES = [
     (1, 1, 1, 1300, 6000, 128, "bf16", True, "dense_f32"),
     (1, 1, 1, 1, 77, 128, "bf16", False, "none"),
     (1, 2, 1, 33, 1, 128, "bf16", True, "none"),
+    # causal work order: with 2 query tiles per head, 32 heads fill each XCD's
+    # range with windows of 4 heads, 16 heads with windows of 2 (8 waves: 5
+    # query tiles per head, windows of 2)
+    (2, 16, 4, 250, 250, 128, "bf16", True, "none"),
+    (1, 16, 16, 200, 230, 128, "bf16", True, "alibi"),
+    (1, 16, 4, 1030, 5150, 128, "bf16", True, "none"),
 ]
 
 
