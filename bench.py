@@ -34,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -117,11 +118,21 @@ def decode_step_bytes(B, Hq, Hkv, Lq, Lk, D, S, elem=2, o_elem=2) -> int:
             + B * Hq * Lq * D * o_elem + B * Hq * Lq * 4)
 
 
+_TOKEN = re.compile(r'("(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\')|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed:
+    what the compiler sees, so that a comment edit leaves the digest alone."""
+    no_comments = _TOKEN.sub(lambda m: m.group(1) if m.group(1) is not None else " ", src)
+    return " ".join(no_comments.split())
+
+
 def source_digest(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -508,7 +519,8 @@ def traffic_table(d):
     out = {"_about": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per "
                      "dispatch, mean over the dispatches of the run), each scaled by the factor that makes the "
                      "same counter read the known size of a plain 1 GiB device copy (bench.py "
-                     "--copy-calibration). source_digest ties an entry to the kernel source it was measured on; "
+                     "--copy-calibration). source_digest ties an entry to the kernel source it was measured on "
+                     "(comments and whitespace aside); "
                      "bench.py reports null traffic once that source changes.",
            "calibration": {"copy_bytes": copy_bytes, "fetch_kib_per_copy": cf, "write_kib_per_copy": cw,
                            "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5)}}

@@ -86,7 +86,7 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     const int hh = lane >> 5;
 
     // 1. S^T = K Q^T, the two 32-key blocks interleaved (two accumulation
-    //    chains); the K operand reads run 8 matrix-core steps ahead
+    //    chains); the K operand reads run ahead of the matrix core (below)
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)

@@ -95,3 +95,13 @@ def test_l2norm_bytes():
     # x read once, y written once, a 4-byte norm per row
     assert bench.l2norm_bytes(32768, 4096, 2, 2) == 32768 * 4096 * 4 + 32768 * 4
     assert bench.l2norm_bytes(8, 4194304, 4, 4) == 8 * 4194304 * 8 + 32
+
+
+def test_source_digest_ignores_comments_only():
+    # the traffic table is keyed on the code the compiler sees: comment and
+    # whitespace edits keep an entry, any change to the code drops it
+    src = 'int a = 1; // one\n/* block\n comment */ const char *s = "// kept";\n'
+    assert bench.code_text(src) == bench.code_text(src.replace("// one", "// other").replace("\n", "\n\n  "))
+    assert bench.code_text(src) != bench.code_text(src.replace("a = 1", "a = 2"))
+    assert "// kept" in bench.code_text(src)
+    assert bench.code_text("x = '/'; /* c */ y") == "x = '/'; y"
