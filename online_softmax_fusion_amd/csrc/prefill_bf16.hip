@@ -455,11 +455,21 @@ hipError_t launch_prefill_t(const FwdParams &p, hipStream_t stream) {
 // causal 8192), and 4-19% slower below that (causal 2048, 4096), with the
 // soft cap (15%), and for a 4096-key sliding window (1%); with only 16 query
 // rows against 32768 keys they are 38% slower (seven of the eight waves idle).
+// A grid of fewer 256-row workgroups than CUs leaves CUs idle that the
+// 128-row grid would use (B1 H8 Lq 2048 Lk 32768: 0.654 vs 0.483 ms), and
+// with one 256-row workgroup per CU the uneven causal tiles finish unevenly
+// (causal B1 H8 L8192: 0.192 vs 0.169 ms) unless rows see 8192 keys or more
+// (causal B1 H16 Lq 4096 Lk 16384: 0.466 vs 0.477 ms).
 int prefill_waves(const FwdParams &p) {
+    constexpr int64_t kCus = 256;
     if (p.D != 128 || bias_cap(p.bias_kind) || p.window) return 4;   // the rule was measured at d = 128
     if (p.Lq < 1024) return 4;   // few rows: most waves of a 256-row tile would idle (Lq = 16: 678 vs 490 us)
     const int64_t avg_keys = p.causal ? (int64_t)p.Lk - ((int64_t)p.Lq - 1) / 2 : (int64_t)p.Lk;
-    return avg_keys >= 4096 ? 8 : 4;
+    if (avg_keys < 4096) return 4;
+    const int64_t blocks8 = (int64_t)p.B * p.Hq * (((int64_t)p.Lq + 255) / 256);
+    if (blocks8 < kCus) return 4;
+    if (p.causal && blocks8 < 2 * kCus && avg_keys < 8192) return 4;
+    return 8;
 }
 
 template <int D, int NW>

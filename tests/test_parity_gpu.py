@@ -76,7 +76,8 @@ PREFILL_CASES = [
     (2, 2, 2, 130, 190, 128, "bf16", False, "alibi"),
     (2, 2, 2, 96, 140, 128, "bf16", False, "dense_f32"),
     (1, 2, 2, 129, 129, 64, "bf16", True, "dense_bf16"),
-    # >= 1024 rows that see >= 4096 keys on average: the eight-wave (256-row) workgroup
+    # >= 1024 rows that see >= 4096 keys on average, on a grid too small for
+    # the eight-wave form (the four-wave kernel over long rows)
     (1, 2, 1, 1100, 4200, 128, "bf16", False, "none"),
     (1, 2, 2, 1030, 4500, 128, "bf16", False, "alibi"),
     (1, 1, 1, 1300, 6000, 128, "bf16", True, "dense_f32"),
@@ -89,6 +90,42 @@ PREFILL_CASES = [
     (1, 16, 16, 200, 230, 128, "bf16", True, "alibi"),
     (1, 16, 4, 1030, 5150, 128, "bf16", True, "none"),
 ]
+
+
+# The eight-wave (256-row) workgroup: >= 1024 rows that see >= 4096 keys on
+# average (>= 8192 when causal), with at least one 256-row workgroup per CU
+# (B * Hq * ceil(Lq / 256) = 320 here).  Compared on sampled rows: the tile
+# edges of every 256-row block, the ragged last block, in every head.  The
+# causal cases run windows of 4 heads (8 heads per XCD).
+EIGHT_WAVE_CASES = [
+    # B, Hq, Hkv, Lq, Lk, causal, bias
+    (1, 64, 16, 1030, 4200, False, "none"),
+    (1, 64, 64, 1030, 4500, False, "alibi"),
+    (1, 64, 16, 1030, 8800, True, "dense_f32"),
+    (1, 64, 8, 1030, 8900, True, "none"),
+]
+
+
+@pytest.mark.parametrize("case", EIGHT_WAVE_CASES, ids=[str(i) for i in range(len(EIGHT_WAVE_CASES))])
+def test_prefill_eight_wave_sampled(case):
+    B, Hq, Hkv, Lq, Lk, causal, bias = case
+    print("eight-wave prefill case", case, flush=True)
+    w = synth.Workload("case8", B, Hq, Hkv, Lq, Lk, 128, "bf16", causal, bias, 29)
+    q, k, v = synth.make_qkv(w)
+    gkw, okw = {}, {}
+    if bias == "alibi":
+        sl = synth.alibi_slopes(Hq)
+        gkw["alibi_slopes"], okw["alibi_slopes"] = sl.cuda(), sl
+    elif bias == "dense_f32":
+        bt = synth.make_dense_bias(w, (Lq, Lk), "f32")   # broadcast over batch and heads
+        gkw["bias"], okw["bias"] = bt.cuda(), bt.float()
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), causal, **gkw)
+    torch.cuda.synchronize()
+    local = sorted({i for t in range(0, Lq, 256) for i in (t, t + 1, t + 127, t + 128, t + 255) if i < Lq} | {Lq - 1})
+    rows = np.array([(b * Hq + h) * Lq + i for b in range(B) for h in range(Hq) for i in local], dtype=np.int64)
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, rows=rows, **okw)
+    compare(o.reshape(-1, 128)[torch.from_numpy(rows).cuda()], lse.reshape(-1)[torch.from_numpy(rows).cuda()],
+            O_ref, L_ref, "bf16", str(case))
 
 
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(i) for i in range(len(PREFILL_CASES))])
