@@ -401,9 +401,10 @@ def time_plan(w):
 
 
 def plan_sweep(causal):
-    """Both forward paths over B 1, 4; Hq/Hkv 8/8, 32/8, 64/8; Lq 1..2048;
+    """The forward paths over B 1, 4; Hq/Hkv 8/8, 32/8, 64/8; Lq 1..2048;
     Lk 4096, 32768 (d = 128, bf16): prefill kernel, split-K at each split
-    count, the planner's choice.  One JSON line per shape on stdout."""
+    count, the prefill kernel over key chunks at each chunk count, the
+    planner's choice.  One JSON line per shape on stdout."""
     import torch
     import synth
     import online_softmax_fusion_amd as attn
@@ -440,8 +441,29 @@ def plan_sweep(causal):
                         if best is None or t < best[1]:
                             best = (S, t)
                     res["best_S"], res["best_splitk_us"] = best[0], round(best[1], 1)
+                    # the prefill kernel over key chunks, then the combine
+                    pblocks = B * Hq * ((Lq + 127) // 128)
+                    pbest = None
+                    for S in (2, 4, 8, 16, 32):
+                        if S > Lk // 512 or pblocks * (S // 2) > 2 * cu:
+                            continue
+                        op = torch.empty((B, Hq, Lq, S, 128), device="cuda")
+                        mp = torch.empty((B, Hq, Lq, S), device="cuda")
+                        lp = torch.empty_like(mp)
+
+                        def run_p():
+                            attn.attn_fwd_prefill_splitk(q, k, v, S, sc, causal, o_part=op, m_part=mp, l_part=lp)
+                            attn.attn_splitk_combine(op, mp, lp, out=o, lse=lse)
+
+                        t = _median_us(run_p)
+                        res["psplit_S%d_us" % S] = round(t, 1)
+                        if pbest is None or t < pbest[1]:
+                            pbest = (S, t)
+                    if pbest is not None:
+                        res["best_pS"], res["best_psplit_us"] = pbest[0], round(pbest[1], 1)
                     plan = attn.attn_fwd_choose_plan(q, k, v, sc, causal)
-                    res["plan"] = "splitk" if plan.method == attn.ATTN_PLAN_SPLITK else "prefill"
+                    res["plan"] = {attn.ATTN_PLAN_SPLITK: "splitk", attn.ATTN_PLAN_PREFILL_SPLIT: "psplit"}.get(
+                        plan.method, "prefill")
                     res["plan_S"] = plan.num_splits
                     print(json.dumps(res), flush=True)
                 del k, v

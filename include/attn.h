@@ -183,23 +183,59 @@ int32_t attn_decode_choose_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq
  * along the keys.
  *
  * attn_fwd_choose_plan picks, from the shapes alone (pure host function):
- *   split-K, when R = B * Hkv * ceil(G * Lq / 32) row blocks fit on the
- *            compute units at once (R <= cu_count), with num_splits from
- *            attn_decode_choose_splits;
+ *   split-K, when Lq <= 16 and R = B * Hkv * ceil(G * Lq / 32) row blocks
+ *            fit on the compute units at once (R <= cu_count), with
+ *            num_splits from attn_decode_choose_splits;
+ *   split prefill, otherwise, when attn_prefill_choose_splits gives two or
+ *            more key chunks (the prefill grid leaves compute units idle, or
+ *            the rows are long enough for chunks of 8192 keys), then the
+ *            combine;
+ *   split-K, otherwise, when R <= cu_count;
  *   prefill, otherwise (and always for fp32 inputs, or shapes the split-K
  *            grid cannot hold).
- * The boundary is measured: on MI355X, over 216 shapes (B 1 and 4; Hq/Hkv
- * 8/8, 32/8, 64/8; Lq 1 to 2048; Lk 4096 and 32768; causal and not) the
- * split-K path is faster in every shape with R <= 256 (1.3x to 16.6x) and
- * slower in every shape with R >= 512 (by 1.1x to 3x).
+ * The rule is measured: on MI355X, over 216 shapes (B 1 and 4; Hq/Hkv 8/8,
+ * 32/8, 64/8; Lq 1 to 2048; Lk 4096 and 32768; causal and not) the planned
+ * path is within 1.093x of the fastest of the three at its best split count
+ * (split-K is the fastest for Lq <= 16; the split prefill beats it by up to
+ * 2.2x from Lq = 64 on, and the plain prefill by up to 1.8x on small grids).
  */
-enum { ATTN_PLAN_PREFILL = 0, ATTN_PLAN_SPLITK = 1 };
+enum { ATTN_PLAN_PREFILL = 0, ATTN_PLAN_SPLITK = 1, ATTN_PLAN_PREFILL_SPLIT = 2 };
 
 typedef struct attn_fwd_plan {
-    int32_t method;                  /* ATTN_PLAN_PREFILL or ATTN_PLAN_SPLITK */
-    int32_t num_splits;              /* split-K: key chunks (1 = grouped rows, no split); prefill: 0 */
+    int32_t method;                  /* ATTN_PLAN_PREFILL, ATTN_PLAN_SPLITK or ATTN_PLAN_PREFILL_SPLIT */
+    int32_t num_splits;              /* split-K and split prefill: key chunks (split-K: 1 = grouped rows,
+                                        no split); prefill: 0 */
     size_t workspace_bytes;          /* device workspace attn_fwd needs for this plan (0 for prefill) */
 } attn_fwd_plan;
+
+/*
+ * attn_fwd_prefill_splitk -- the prefill kernel over key chunks (Neptune
+ * notes, section 6: partial results per chunk, merged afterwards): a grid of
+ * (128-row query tile, key chunk) workgroups, for grids too small to occupy
+ * the device over the query rows alone.  Chunk s holds keys
+ *     [s*C, min((s+1)*C, Lk)),  C = 64 * ceil(Lk / (64 * num_splits))
+ * (whole 64-key tiles; trailing chunks may be empty).  The partials have the
+ * layout and meaning of attn_fwd_decode_splitk's (o_part [B, Hq, Lq,
+ * num_splits, D] not normalised, m_part and l_part [B, Hq, Lq, num_splits],
+ * m in natural units; a row that sees no key of a chunk gets m = -inf, l = 0,
+ * o = 0), so attn_splitk_combine finishes the forward.  Arguments as for
+ * attn_fwd_prefill (o, o_strides and lse are not used); bf16 inputs only
+ * (ATTN_ERR_UNSUPPORTED otherwise); 1 <= num_splits <= 65535.  The buffers
+ * are contiguous device fp32 arrays owned by the caller (o_part 16-byte
+ * aligned); nothing is allocated.
+ */
+attn_status attn_fwd_prefill_splitk(const attn_fwd_args *a, int32_t num_splits,
+                                    float *o_part, float *m_part, float *l_part, void *stream);
+
+/*
+ * attn_prefill_choose_splits -- key chunks for attn_fwd_prefill_splitk (pure
+ * host function): enough (query tile, chunk) workgroups for two per compute
+ * unit, B * Hq * ceil(Lq / 128) * num_splits >= 2 * cu_count (<= 0: 256),
+ * with at least 1024 keys per chunk; when the unsplit grid already has a
+ * workgroup per compute unit, only if the chunks hold 8192 keys or more.
+ * Returns 1 (no split) or the chunk count.
+ */
+int32_t attn_prefill_choose_splits(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int32_t cu_count);
 
 /*
  * attn_fwd_choose_plan -- the plan attn_fwd runs for `a` on a device with

@@ -30,7 +30,7 @@ __all__ = [
     "attn_splitk_combine", "attn_decode_choose_splits", "attn_decode_partial_bytes",
     "attn_device_cu_count", "prefill", "decode", "chunk_length", "AttnFwdArgs", "AttnBwdArgs", "attn_bwd",
     "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_choose_plan", "AttnFwdPlan", "ATTN_PLAN_PREFILL",
-    "ATTN_PLAN_SPLITK", "L2NormArgs", "l2norm_rows", "l2norm_choose_splits", "l2norm_workspace_bytes",
+    "ATTN_PLAN_SPLITK", "ATTN_PLAN_PREFILL_SPLIT", "attn_fwd_prefill_splitk", "attn_prefill_choose_splits", "L2NormArgs", "l2norm_rows", "l2norm_choose_splits", "l2norm_workspace_bytes",
     "l2norm_max_onepass",
 ]
 
@@ -41,7 +41,7 @@ _LIB = None
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, 1, 2, 3, 4
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_BIAS_NONE, ATTN_BIAS_DENSE, ATTN_BIAS_ALIBI = 0, 1, 2
-ATTN_PLAN_PREFILL, ATTN_PLAN_SPLITK = 0, 1
+ATTN_PLAN_PREFILL, ATTN_PLAN_SPLITK, ATTN_PLAN_PREFILL_SPLIT = 0, 1, 2
 
 _I64x3 = ctypes.c_int64 * 3
 _I64x4 = ctypes.c_int64 * 4
@@ -120,6 +120,10 @@ def load_library():
     lib.attn_fwd_prefill.restype = ctypes.c_int
     lib.attn_fwd_decode_splitk.argtypes = [P, i32, vp, vp, vp, vp]
     lib.attn_fwd_decode_splitk.restype = ctypes.c_int
+    lib.attn_fwd_prefill_splitk.argtypes = [P, i32, vp, vp, vp, vp]
+    lib.attn_fwd_prefill_splitk.restype = ctypes.c_int
+    lib.attn_prefill_choose_splits.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_prefill_choose_splits.restype = i32
     lib.attn_splitk_combine.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, vp, i32,
                                         ctypes.POINTER(ctypes.c_int64), vp, vp]
     lib.attn_splitk_combine.restype = ctypes.c_int
@@ -352,6 +356,46 @@ def attn_fwd_decode_splitk(q, k, v, num_splits: int, scale: Optional[float] = No
     return o_part, m_part, l_part
 
 
+def prefill_chunk_length(Lk: int, num_splits: int) -> int:
+    """Keys per chunk of the split prefill: 64 * ceil(Lk / (64 * num_splits)) (include/attn.h)."""
+    per = -(-Lk // (64 * num_splits))
+    return 64 * max(per, 1)
+
+
+def attn_fwd_prefill_splitk(q, k, v, num_splits: int, scale: Optional[float] = None, causal: bool = False, *,
+                            bias=None, alibi_slopes=None, o_part=None, m_part=None, l_part=None,
+                            softcap: float = 0.0, window: Optional[Tuple[int, int]] = None):
+    """Prefill over key chunks: partials (o [B,Hq,Lq,S,D], m [B,Hq,Lq,S], l [B,Hq,Lq,S]) in fp32,
+    in the layout of attn_fwd_decode_splitk, for attn_splitk_combine."""
+    lib = load_library()
+    _check_4d("q", q)
+    B, Hq, Lq, D = q.shape
+    S = int(num_splits)
+    dev = q.device
+    if o_part is None:
+        o_part = torch.empty((B, Hq, Lq, S, D), dtype=torch.float32, device=dev)
+    if m_part is None:
+        m_part = torch.empty((B, Hq, Lq, S), dtype=torch.float32, device=dev)
+    if l_part is None:
+        l_part = torch.empty((B, Hq, Lq, S), dtype=torch.float32, device=dev)
+    for name, t, n in (("o_part", o_part, B * Hq * Lq * S * D), ("m_part", m_part, B * Hq * Lq * S),
+                       ("l_part", l_part, B * Hq * Lq * S)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError("%s must be a contiguous GPU fp32 tensor of %d elements" % (name, n))
+        _on(dev, name, t)
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, softcap=softcap, window=window)
+    with torch.cuda.device(dev):
+        st = lib.attn_fwd_prefill_splitk(ctypes.byref(a), S, _ptr(o_part), _ptr(m_part), _ptr(l_part),
+                                         _stream(dev))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_prefill_splitk")
+    return o_part, m_part, l_part
+
+
+def attn_prefill_choose_splits(B: int, Hq: int, Lq: int, Lk: int, cu_count: int = 0) -> int:
+    return int(load_library().attn_prefill_choose_splits(B, Hq, Lq, Lk, cu_count))
+
+
 def attn_splitk_combine(o_part, m_part, l_part, *, out=None, out_dtype=torch.bfloat16, lse=None,
                         return_lse: bool = True):
     """Split-K global step: (O [B,Hq,Lq,D], LSE [B,Hq,Lq]) from the partials."""
@@ -496,8 +540,8 @@ def attn_fwd_choose_plan(q, k, v, scale: Optional[float] = None, causal: bool = 
 def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bias=None, alibi_slopes=None,
              out=None, out_dtype: Optional[torch.dtype] = None, lse=None, return_lse: bool = True,
              softcap: float = 0.0, window: Optional[Tuple[int, int]] = None, workspace=None):
-    """Forward with the automatically chosen parallel dimensions (prefill, or
-    grouped split-K plus combine).  Same arguments and results as
+    """Forward with the automatically chosen parallel dimensions (prefill,
+    grouped split-K plus combine, or prefill over key chunks plus combine).  Same arguments and results as
     ``attn_fwd_prefill``; ``workspace`` may be a GPU byte tensor to reuse (a
     new one of the plan's size is allocated otherwise)."""
     lib = load_library()

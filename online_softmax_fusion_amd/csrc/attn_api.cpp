@@ -112,6 +112,22 @@ int32_t chunk_len(int64_t Lk, int32_t S) {
     return (int32_t)(per < 1 ? 32 : per * 32);
 }
 
+// split prefill: enough (query tile, key chunk) workgroups for kPrefillSplitSlots
+// per compute unit, with at least kPrefillSplitMinKeys keys per chunk; on a
+// prefill grid that already gives every compute unit a workgroup, only chunks
+// of kPrefillSplitLongChunk keys or more (the combine's cost is paid per row)
+constexpr int64_t kPrefillSplitSlots = 2;
+constexpr int64_t kPrefillSplitMinKeys = 1024;
+constexpr int64_t kPrefillSplitLongChunk = 8192;
+// grouped split-K only for decode-like query lengths
+constexpr int64_t kSplitKMaxLq = 16;
+
+// keys per chunk of the split prefill: whole 64-key tiles
+int64_t prefill_chunk_len(int64_t Lk, int32_t num_splits) {
+    const int64_t per = (Lk + 64 * (int64_t)num_splits - 1) / (64 * (int64_t)num_splits);
+    return 64 * (per > 0 ? per : 1);
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,6 +187,40 @@ attn_status attn_fwd_decode_splitk(const attn_fwd_args *a, int32_t num_splits, f
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err = (a->dtype == ATTN_BF16) ? attn::launch_decode_bf16(p, s) : attn::launch_rows_f32(p, 1, s);
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd_prefill_splitk(const attn_fwd_args *a, int32_t num_splits, float *o_part, float *m_part,
+                                    float *l_part, void *stream) {
+    attn_status st = check_common(a);   // o, o_strides and lse are not used
+    if (st != ATTN_OK) return st;
+    if (num_splits < 1 || num_splits > 65535) return ATTN_ERR_INVALID_ARG;
+    if (a->B * a->Hq * a->Lq > 0) {
+        if (o_part == nullptr || m_part == nullptr || l_part == nullptr) return ATTN_ERR_INVALID_ARG;
+        if (!aligned(o_part, 16) || !aligned(m_part, 4) || !aligned(l_part, 4)) return ATTN_ERR_INVALID_ARG;
+    }
+    if (a->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (a->B * a->Hq * a->Lq == 0) return ATTN_OK;
+    FwdParams p = make_params(a);
+    p.num_splits = num_splits;
+    p.chunk = (int)prefill_chunk_len(a->Lk, num_splits);
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+    hipError_t err = attn::launch_prefill_part_bf16(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int32_t attn_prefill_choose_splits(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int32_t cu_count) {
+    if (B < 1 || Hq < 1 || Lq < 1 || Lk < 1) return 1;
+    const int64_t cu = cu_count > 0 ? cu_count : 256;
+    const int64_t blocks = B * Hq * ((Lq + 127) / 128);
+    int64_t S = (kPrefillSplitSlots * cu + blocks - 1) / blocks;
+    const int64_t max_by_len = Lk / kPrefillSplitMinKeys;
+    if (S > max_by_len) S = max_by_len;
+    if (S > 65535) S = 65535;
+    if (S < 2) return 1;
+    if (blocks >= cu && prefill_chunk_len(Lk, (int32_t)S) < kPrefillSplitLongChunk) return 1;
+    return (int32_t)S;
 }
 
 attn_status attn_splitk_combine(const float *o_part, const float *m_part, const float *l_part, int64_t B,
@@ -289,7 +339,16 @@ attn_status attn_fwd_choose_plan(const attn_fwd_args *a, int32_t cu_count, attn_
     plan->method = ATTN_PLAN_PREFILL;
     plan->num_splits = 0;
     plan->workspace_bytes = 0;
-    if (a->dtype == ATTN_BF16 && R > 0 && R <= cu && a->Lk > 0 && a->B * a->Hkv <= 65535 && rblocks <= 65535) {
+    if (a->dtype != ATTN_BF16 || a->Lk <= 0 || R <= 0) return ATTN_OK;
+    const bool splitk_fits = R <= cu && a->B * a->Hkv <= 65535 && rblocks <= 65535;
+    const int32_t PS = a->Lq > kSplitKMaxLq || !splitk_fits
+                           ? attn_prefill_choose_splits(a->B, a->Hq, a->Lq, a->Lk, (int32_t)cu)
+                           : 1;
+    if (PS >= 2) {
+        plan->method = ATTN_PLAN_PREFILL_SPLIT;
+        plan->num_splits = PS;
+        plan->workspace_bytes = attn_decode_partial_bytes(a->B, a->Hq, a->Lq, a->D, PS);
+    } else if (splitk_fits) {
         const int32_t S = attn_decode_choose_splits(a->B, a->Hq, a->Hkv, a->Lq, a->Lk, (int32_t)cu);
         plan->method = ATTN_PLAN_SPLITK;
         plan->num_splits = S;
@@ -314,7 +373,8 @@ attn_status attn_fwd(const attn_fwd_args *a, void *workspace, size_t workspace_b
     float *o_part = static_cast<float *>(workspace);
     float *m_part = o_part + parts * a->D;
     float *l_part = m_part + parts;
-    st = attn_fwd_decode_splitk(a, plan.num_splits, o_part, m_part, l_part, stream);
+    st = plan.method == ATTN_PLAN_SPLITK ? attn_fwd_decode_splitk(a, plan.num_splits, o_part, m_part, l_part, stream)
+                                         : attn_fwd_prefill_splitk(a, plan.num_splits, o_part, m_part, l_part, stream);
     if (st != ATTN_OK) return st;
     return attn_splitk_combine(o_part, m_part, l_part, a->B, a->Hq, a->Lq, a->D, plan.num_splits, a->o, a->o_dtype,
                                a->o_strides, a->lse, stream);

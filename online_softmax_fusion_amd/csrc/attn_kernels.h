@@ -123,6 +123,9 @@ struct L2Params {
 
 // bf16 prefill with the rolling update (matrix cores, D in {64, 128}).
 hipError_t launch_prefill_bf16(const FwdParams &p, hipStream_t stream);
+// split-K prefill: key chunks of p.chunk keys (a multiple of 64), p.num_splits of them,
+// partials to p.o_part / p.m_part / p.l_part in the decode kernel's layout
+hipError_t launch_prefill_part_bf16(const FwdParams &p, hipStream_t stream);
 // bf16 split-K decode partials (matrix cores, D in {64, 128}).
 hipError_t launch_decode_bf16(const FwdParams &p, hipStream_t stream);
 // fp32 path: one wavefront per query row; partial != 0 writes split-K partials.

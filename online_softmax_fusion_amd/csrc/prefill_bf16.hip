@@ -240,8 +240,11 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, co
         }                                                                                                       \
     } while (0)
 
-template <int D, int NW, int BIAS, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(FwdParams p) {
+// The body of both prefill kernels.  PART: key chunk blockIdx.y of p.chunk
+// keys (a multiple of the key tile), written as split-K partials (O not
+// normalised, m in natural units, l) for the combine instead of O and LSE.
+template <int D, int NW, int BIAS, bool OUT_BF16, bool PART>
+__device__ __forceinline__ void prefill_body(const FwdParams &p) {
     using C = TileCfg<D>;
     constexpr int BR = 32 * NW;          // query rows per workgroup
     constexpr int BC = C::BC;
@@ -293,6 +296,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(FwdParams
     if (rlast >= q0 && gjmax1 >= gjmin0) {
         t_first = gjmin0 / BC;
         t_end = gjmax1 / BC + 1;
+    }
+    if constexpr (PART) {
+        const int c0 = (int)blockIdx.y * (p.chunk / BC);
+        t_first = max(t_first, c0);
+        t_end = min(t_end, c0 + p.chunk / BC);
     }
     const int u_first = max(t_first, (gjmin1 + BC - 1) / BC);
     const int u_end = min(t_end, gjmax0 >= 0 ? (gjmax0 + 1) / BC : 0);
@@ -403,6 +411,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(FwdParams
 
     // epilogue
     const float l_tot = xor32_sum(l_run);
+    if constexpr (PART) {
+        if (qrow < p.Lq) {
+            const int64_t prow = (((int64_t)b * p.Hq + h) * p.Lq + qrow) * p.num_splits + blockIdx.y;
+            float *op = p.o_part + prow * D;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<f32x4 *>(op + db * 32 + i * 8 + hh * 4) =
+                        f32x4{oacc[db][4 * i], oacc[db][4 * i + 1], oacc[db][4 * i + 2], oacc[db][4 * i + 3]};
+            if (hh == 0) {
+                p.m_part[prow] = (m_run == -INFINITY) ? -INFINITY : m_run * kLn2;
+                p.l_part[prow] = l_tot;
+            }
+        }
+        return;
+    }
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     if (qrow < p.Lq) {
         const int64_t obase = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sl;
@@ -426,6 +451,45 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(FwdParams
             const float lse = (l_tot > 0.f) ? m_run * kLn2 + logf(l_tot) : -INFINITY;
             p.lse[((int64_t)b * p.Hq + h) * p.Lq + qrow] = lse;
         }
+    }
+}
+
+template <int D, int NW, int BIAS, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(FwdParams p) {
+    prefill_body<D, NW, BIAS, OUT_BF16, false>(p);
+}
+
+// split-K form: grid (query tiles, key chunks), four waves
+template <int D, int BIAS>
+__global__ __launch_bounds__(256, 2) void prefill_part_kernel(FwdParams p) {
+    prefill_body<D, 4, BIAS, false, true>(p);
+}
+
+template <int D, int BIAS>
+hipError_t launch_prefill_part_t(const FwdParams &p, hipStream_t stream) {
+    const int64_t nqt = (p.Lq + 127) / 128;
+    const int64_t blocks = nqt * (int64_t)p.B * p.Hq;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffff || p.num_splits < 1 || p.num_splits > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_part_kernel<D, BIAS>), dim3((unsigned)blocks, (unsigned)p.num_splits), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_part_d(const FwdParams &p, hipStream_t stream) {
+    const int kind = (p.bias_kind == kBiasNone && !(p.scale_log2 > 0.f)) ? kBiasNoneScaled : p.bias_kind;
+    switch (kind) {
+        case kBiasNone: return launch_prefill_part_t<D, kBiasNone>(p, stream);
+        case kBiasNoneScaled: return launch_prefill_part_t<D, kBiasNoneScaled>(p, stream);
+        case kBiasAlibi: return launch_prefill_part_t<D, kBiasAlibi>(p, stream);
+        case kBiasDenseF32: return launch_prefill_part_t<D, kBiasDenseF32>(p, stream);
+        case kBiasDenseBf16: return launch_prefill_part_t<D, kBiasDenseBf16>(p, stream);
+        case kBiasNoneCap: return launch_prefill_part_t<D, kBiasNoneCap>(p, stream);
+        case kBiasAlibiCap: return launch_prefill_part_t<D, kBiasAlibiCap>(p, stream);
+        case kBiasDenseF32Cap: return launch_prefill_part_t<D, kBiasDenseF32Cap>(p, stream);
+        case kBiasDenseBf16Cap: return launch_prefill_part_t<D, kBiasDenseBf16Cap>(p, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 
@@ -504,6 +568,13 @@ hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
 hipError_t launch_prefill_bf16(const FwdParams &p, hipStream_t stream) {
     if (p.D == 128) return launch_prefill_d<128>(p, stream);
     if (p.D == 64) return launch_prefill_d<64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_part_bf16(const FwdParams &p, hipStream_t stream) {
+    if (p.chunk < 64 || p.chunk % 64 != 0) return hipErrorInvalidValue;   // whole key tiles per chunk
+    if (p.D == 128) return launch_prefill_part_d<128>(p, stream);
+    if (p.D == 64) return launch_prefill_part_d<64>(p, stream);
     return hipErrorInvalidValue;
 }
 

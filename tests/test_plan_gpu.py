@@ -22,10 +22,10 @@ def need_gpu():
 CASES = [
     # B, Hq, Hkv, Lq, Lk, causal, bias, softcap, window, expected plan
     (1, 8, 8, 16, 4096, False, "none", 0.0, None, attn.ATTN_PLAN_SPLITK),
-    (1, 32, 8, 100, 3000, True, "none", 0.0, None, attn.ATTN_PLAN_SPLITK),     # Lq < Lk, end-aligned
+    (1, 32, 8, 100, 3000, True, "none", 0.0, None, attn.ATTN_PLAN_PREFILL_SPLIT),  # Lq < Lk, end-aligned
     (2, 4, 4, 700, 700, True, "alibi", 0.0, None, attn.ATTN_PLAN_SPLITK),     # 176 row blocks, 2 chunks
-    (1, 8, 2, 33, 5000, False, "none", 20.0, (300, 40), attn.ATTN_PLAN_SPLITK),
-    (1, 16, 4, 64, 2048, True, "dense_f32", 0.0, (511, -1), attn.ATTN_PLAN_SPLITK),
+    (1, 8, 2, 33, 5000, False, "none", 20.0, (300, 40), attn.ATTN_PLAN_PREFILL_SPLIT),
+    (1, 16, 4, 64, 2048, True, "dense_f32", 0.0, (511, -1), attn.ATTN_PLAN_PREFILL_SPLIT),
     (4, 16, 16, 300, 300, True, "none", 0.0, None, attn.ATTN_PLAN_PREFILL),
     (2, 8, 8, 1100, 1500, False, "alibi", 0.0, None, attn.ATTN_PLAN_PREFILL),
 ]
