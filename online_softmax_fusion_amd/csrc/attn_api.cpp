@@ -200,9 +200,11 @@ attn_status attn_fwd_prefill_splitk(const attn_fwd_args *a, int32_t num_splits, 
     }
     if (a->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (a->B * a->Hq * a->Lq == 0) return ATTN_OK;
+    const int64_t chunk = prefill_chunk_len(a->Lk, num_splits);
+    if (chunk > kIntMax) return ATTN_ERR_UNSUPPORTED;   // the kernel holds key positions in 32 bits
     FwdParams p = make_params(a);
     p.num_splits = num_splits;
-    p.chunk = (int)prefill_chunk_len(a->Lk, num_splits);
+    p.chunk = (int)chunk;
     p.o_part = o_part;
     p.m_part = m_part;
     p.l_part = l_part;
