@@ -19,8 +19,11 @@ Default run (N = 1):
   * plan leg -- attn_fwd (automatic choice of parallel dimensions) on a
     short-query GQA shape (B=1, Hq=32, Hkv=8, Lq=16, Lk=32768): the plan it
     picks, its time, and the prefill kernel's time on the same problem.
-    Reported under "plan".  `--plan-sweep` times both paths over the shape
-    grid that set the planner's boundary (one JSON line per shape).
+    Reported under "plan"; the same for a small-grid prefill with long rows
+    (B=1, H=8, Lq=2048, Lk=32768, causal), where the plan splits the keys of
+    the prefill kernel, under "plan_long_keys".  `--plan-sweep` times the
+    three paths over the shape grid that set the planner's rule (one JSON
+    line per shape).
   * l2norm leg -- the row L2 norm (the same repair algebra on a sum of
     squares): 32768 rows of 4096 bf16 values in one pass, and 8 rows of
     4194304 fp32 values split over the row.  Reported under "l2norm" in
@@ -393,9 +396,10 @@ def time_plan(w):
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
     t_fwd = _median_us(lambda: attn.attn_fwd(q, k, v, sc, w.causal, out=o, lse=lse, workspace=ws), 20)
     t_pf = _median_us(lambda: attn.attn_fwd_prefill(q, k, v, sc, w.causal, out=o, lse=lse), 20)
-    log("plan: %s -> %s S=%d, %.1f us (prefill kernel %.1f us)" %
-        (w.name, "split-K" if plan.method == attn.ATTN_PLAN_SPLITK else "prefill", plan.num_splits, t_fwd, t_pf))
-    return {"workload": w.name, "method": "splitk" if plan.method == attn.ATTN_PLAN_SPLITK else "prefill",
+    method = {attn.ATTN_PLAN_SPLITK: "splitk", attn.ATTN_PLAN_PREFILL_SPLIT: "split_prefill"}.get(plan.method,
+                                                                                                "prefill")
+    log("plan: %s -> %s S=%d, %.1f us (prefill kernel %.1f us)" % (w.name, method, plan.num_splits, t_fwd, t_pf))
+    return {"workload": w.name, "method": method,
             "splits": plan.num_splits, "attn_fwd_us": round(t_fwd, 1), "prefill_kernel_us": round(t_pf, 1),
             "speedup": round(t_pf / t_fwd, 2)}
 
@@ -649,6 +653,7 @@ def main():
     step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup, args.warm_seconds)
     d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup, args.warm_seconds)
     plan_res = time_plan(synth.PLAN_SHORT_GQA)
+    plan_long_res = time_plan(synth.PLAN_LONG_KEYS)
     l2_res = [time_l2norm(w, args.steps, args.warmup, args.warm_seconds) for w in (synth.L2N_ROWS, synth.L2N_LONG)]
     wb = None if args.backward == "none" else synth.WORKLOADS[args.backward or synth.BWD_PREFILL.name]
     if wb is not None:
@@ -688,6 +693,7 @@ def main():
                                 "traffic": measured_traffic("decode_bf16_kernel", wd.name, DECODE_SOURCES)}},
     }
     result["plan"] = plan_res
+    result["plan_long_keys"] = plan_long_res
     result["l2norm"] = l2_res
     if wb is not None:
         b_kern_tflops = b_flops / b_kern_s / 1e12

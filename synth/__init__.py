@@ -94,8 +94,14 @@ BWD_PREFILL = Workload("bwd-noncausal-bf16-B4-H32-L4096-d128", 4, 32, 32, 4096, 
 PLAN_SHORT_GQA = Workload("short-gqa-bf16-B1-Hq32-Hkv8-Lq16-Lk32768-d128", 1, 32, 8, 16, 32768, 128,
                           "bf16", True, "none", 1009)
 
+# A small-grid prefill (2048 new rows of 8 heads against a 32768-key cache):
+# 128 query tiles of 128 rows leave half of 256 CUs idle unless the keys are
+# split as well.
+PLAN_LONG_KEYS = Workload("long-keys-prefill-bf16-B1-H8-Lq2048-Lk32768-d128", 1, 8, 8, 2048, 32768, 128,
+                          "bf16", True, "none", 1013)
+
 WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PREFILL, C5_DECODE,
-                                 SOFTCAP_PREFILL, WINDOW_PREFILL, BWD_PREFILL, PLAN_SHORT_GQA)}
+                                 SOFTCAP_PREFILL, WINDOW_PREFILL, BWD_PREFILL, PLAN_SHORT_GQA, PLAN_LONG_KEYS)}
 
 
 @dataclass(frozen=True)
