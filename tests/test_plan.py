@@ -123,3 +123,24 @@ def test_plan_validates(lib):
     a = args(1, 8, 8, 16, 4096)
     a.o = None
     assert lib.attn_fwd(ctypes.byref(a), None, 0, None) == INVALID
+
+
+def test_prefill_split_count_contract(lib):
+    # include/attn.h: enough (query tile, chunk) workgroups for two per CU, at
+    # least 1024 keys per chunk, and on a grid with a workgroup per CU only
+    # chunks of 8192 keys or more; 1 means no split
+    for cu in (0, 80, 256):
+        c = cu if cu > 0 else 256
+        for B, Hq in ((1, 1), (1, 8), (2, 16), (4, 64)):
+            for Lq in (1, 100, 128, 1000, 4096):
+                for Lk in (1, 1023, 2048, 5000, 32768, 100000):
+                    S = lib.attn_prefill_choose_splits(B, Hq, Lq, Lk, cu)
+                    blocks = B * Hq * -(-Lq // 128)
+                    assert S >= 1
+                    if S == 1:
+                        continue
+                    chunk = attn.prefill_chunk_length(Lk, S)
+                    assert Lk // S >= 1024
+                    assert blocks * (S - 1) < 2 * c   # no more chunks than two workgroups per CU need
+                    assert blocks < c or chunk >= 8192
+    assert lib.attn_prefill_choose_splits(0, 8, 128, 4096, 256) == 1
