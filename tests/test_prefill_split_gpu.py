@@ -91,3 +91,35 @@ def test_prefill_splitk_rejects_fp32():
     w, q, k, v, _, _ = inputs(1, 1, 1, 64, 128, 64, "f32", False, "none")
     with pytest.raises(attn.AttnError):
         attn.attn_fwd_prefill_splitk(q.cuda(), k.cuda(), v.cuda(), 2, w.softmax_scale(), False)
+
+
+def test_attn_fwd_split_prefill_graph_replay():
+    """attn_fwd on the split-prefill plan (prefill over key chunks + combine)
+    captured in a HIP graph gives the eager result on every replay, with other
+    eager work between replays."""
+    w, q, k, v, _, _ = inputs(1, 8, 8, 1100, 5000, 128, "bf16", True, "none", seed=13)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    sc = w.softmax_scale()
+    plan = attn.attn_fwd_choose_plan(q, k, v, sc, True)
+    assert plan.method == attn.ATTN_PLAN_PREFILL_SPLIT
+    ws = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 8, 1100), dtype=torch.float32, device="cuda")
+
+    def step():
+        attn.attn_fwd(q, k, v, sc, True, out=o, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = o.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        o.zero_()
+        lse.zero_()
+        attn.attn_fwd(q * 0.5, k, v, sc, True)   # unrelated eager work on the same plan
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), "replay %d" % r
