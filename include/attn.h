@@ -38,8 +38,8 @@
  *                partials are fp32.  fp32 inputs are computed in fp32.
  *   Pointers     every tensor pointer is a DEVICE pointer owned by the caller;
  *                the library never allocates, frees or synchronises, keeps no
- *                state except a per-device cache of the compute-unit count, and
- *                enqueues its kernels on the given HIP stream (a hipStream_t
+ *                state except a per-device cache of the compute-unit and XCD
+ *                counts, and enqueues its kernels on the given HIP stream (a hipStream_t
  *                passed as void*, NULL = the null stream).  Calls return as soon
  *                as the kernels are enqueued.  Calls are thread-safe.
  *   Alignment    q, k, v and o base pointers must be 16-byte aligned and every
@@ -47,8 +47,12 @@
  *   Errors       arguments are checked on the host before anything is
  *                enqueued; a failed check returns ATTN_ERR_INVALID_ARG (bad
  *                value) or ATTN_ERR_UNSUPPORTED (valid but not implemented:
- *                D not in {64, 128}, dtype combination, alignment) and enqueues
- *                nothing.  A launch failure returns ATTN_ERR_HIP.  No C++
+ *                D not in {64, 128}, dtype combination, alignment; sizes
+ *                beyond what the kernels hold: any of B, H, L, D above
+ *                2^31 - 1, or products of them past the kernels' 32-bit
+ *                grids) and enqueues nothing.  A launch failure returns
+ *                ATTN_ERR_HIP; the thread's HIP error state is cleared before
+ *                the launch, so the error is the call's own.  No C++
  *                exception crosses this interface.
  */
 #ifndef ATTN_MI355X_H
@@ -260,6 +264,16 @@ size_t attn_decode_partial_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, i
 
 /* attn_device_cu_count -- compute units of HIP device `device` (cached); <= 0 on error. */
 int32_t attn_device_cu_count(int32_t device);
+
+/*
+ * attn_device_xcd_count -- accelerator complex dies (XCDs) of HIP device
+ * `device` (cached; 1 when the runtime reports none); <= 0 on error.  Each
+ * XCD has its own L2 cache and the hardware deals workgroups to the XCDs in
+ * turn; the kernels order their work by this count so that the K/V of one
+ * head stays in one XCD's L2.  Every launching call reads both counts of the
+ * current device.
+ */
+int32_t attn_device_xcd_count(int32_t device);
 
 /*
  * attn_validate_prefill / attn_validate_decode -- the host-side argument

@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "AttnError", "load_library", "library_path", "attn_fwd_prefill", "attn_fwd_decode_splitk",
     "attn_splitk_combine", "attn_decode_choose_splits", "attn_decode_partial_bytes",
-    "attn_device_cu_count", "prefill", "decode", "chunk_length", "AttnFwdArgs", "AttnBwdArgs", "attn_bwd",
+    "attn_device_cu_count", "attn_device_xcd_count", "prefill", "decode", "chunk_length", "AttnFwdArgs", "AttnBwdArgs", "attn_bwd",
     "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_choose_plan", "AttnFwdPlan", "ATTN_PLAN_PREFILL",
     "ATTN_PLAN_SPLITK", "ATTN_PLAN_PREFILL_SPLIT", "attn_fwd_prefill_splitk", "attn_prefill_choose_splits", "L2NormArgs", "l2norm_rows", "l2norm_choose_splits", "l2norm_workspace_bytes",
     "l2norm_max_onepass",
@@ -133,6 +133,8 @@ def load_library():
     lib.attn_decode_partial_bytes.restype = ctypes.c_size_t
     lib.attn_device_cu_count.argtypes = [i32]
     lib.attn_device_cu_count.restype = i32
+    lib.attn_device_xcd_count.argtypes = [i32]
+    lib.attn_device_xcd_count.restype = i32
     lib.attn_validate_prefill.argtypes = [P]
     lib.attn_validate_prefill.restype = ctypes.c_int
     lib.attn_validate_decode.argtypes = [P, i32, vp, vp, vp]
@@ -436,6 +438,10 @@ def attn_decode_partial_bytes(B: int, Hq: int, Lq: int, D: int, num_splits: int)
 
 def attn_device_cu_count(device: int = 0) -> int:
     return int(load_library().attn_device_cu_count(device))
+
+
+def attn_device_xcd_count(device: int = 0) -> int:
+    return int(load_library().attn_device_xcd_count(device))
 
 
 def decode(q, k, v, num_splits: Optional[int] = None, scale: Optional[float] = None, causal: bool = False, *,

@@ -22,6 +22,30 @@ int64_t elem_size(int32_t dt) { return dt == ATTN_BF16 ? 2 : 4; }
 
 bool valid_dtype(int32_t dt) { return dt == ATTN_F32 || dt == ATTN_BF16; }
 
+// a * b * c, false when the product of these non-negative values leaves int64
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t &out) {
+    int64_t t;
+    return !__builtin_mul_overflow(a, b, &t) && !__builtin_mul_overflow(t, c, &out);
+}
+
+// ceil(a / b) for 0 <= a and b >= 1, without forming a + b - 1
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+// a * b for non-negative values, saturating at INT64_MAX
+int64_t sat_mul(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
+// Launches `fn` with the HIP error state cleared first, so that a launch
+// error reported afterwards belongs to this call and not to earlier,
+// unrelated work on the thread.
+template <class F>
+attn_status launch(F fn) {
+    (void)hipGetLastError();
+    return fn() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 // Checks shared by prefill and decode.
 attn_status check_common(const attn_fwd_args *a) {
     if (a == nullptr) return ATTN_ERR_INVALID_ARG;
@@ -35,10 +59,15 @@ attn_status check_common(const attn_fwd_args *a) {
         if (a->q_strides[t] < 0 || a->k_strides[t] < 0 || a->v_strides[t] < 0) return ATTN_ERR_INVALID_ARG;
     if (a->bias_kind != ATTN_BIAS_NONE && a->bias_kind != ATTN_BIAS_DENSE && a->bias_kind != ATTN_BIAS_ALIBI)
         return ATTN_ERR_INVALID_ARG;
-
-    const int64_t rows = a->B * a->Hq * a->Lq;
+    // every size is held in 32 bits by the kernels; bounding each one first
+    // also keeps the products below from overflowing
+    if (a->B > kIntMax || a->Hq > kIntMax || a->Hkv > kIntMax || a->Lq > kIntMax || a->Lk > kIntMax ||
+        a->D > kIntMax)
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t rows = 0, kv_rows = 0;
+    if (!mul3(a->B, a->Hq, a->Lq, rows) || !mul3(a->B, a->Hkv, a->Lk, kv_rows)) return ATTN_ERR_UNSUPPORTED;
     const bool any_q = rows > 0;
-    const bool any_kv = a->B * a->Hkv * a->Lk > 0;
+    const bool any_kv = kv_rows > 0;
     if (any_q && a->q == nullptr) return ATTN_ERR_INVALID_ARG;
     if (any_q && any_kv && (a->k == nullptr || a->v == nullptr)) return ATTN_ERR_INVALID_ARG;
     if (a->bias_kind == ATTN_BIAS_DENSE) {
@@ -104,11 +133,24 @@ FwdParams make_params(const attn_fwd_args *a) {
     return p;
 }
 
+// Compute units and XCDs of the current device, for the kernels' work order
+// and the launch rules that depend on how many workgroups the device holds.
+attn_status device_topology(FwdParams &p) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    const int32_t cus = attn_device_cu_count(device);
+    const int32_t xcds = attn_device_xcd_count(device);
+    if (cus <= 0 || xcds <= 0) return ATTN_ERR_HIP;
+    p.num_cus = cus;
+    p.num_xcds = xcds;
+    return ATTN_OK;
+}
+
 // rows of one workspace array, rounded up to 16 bytes
 int64_t bwd_rows_padded(int64_t rows) { return (rows + 3) / 4 * 4; }
 
 int32_t chunk_len(int64_t Lk, int32_t S) {
-    const int64_t per = (Lk + (int64_t)S * 32 - 1) / ((int64_t)S * 32);
+    const int64_t per = ceil_div(Lk, (int64_t)S * 32);
     return (int32_t)(per < 1 ? 32 : per * 32);
 }
 
@@ -124,7 +166,7 @@ constexpr int64_t kSplitKMaxLq = 16;
 
 // keys per chunk of the split prefill: whole 64-key tiles
 int64_t prefill_chunk_len(int64_t Lk, int32_t num_splits) {
-    const int64_t per = (Lk + 64 * (int64_t)num_splits - 1) / (64 * (int64_t)num_splits);
+    const int64_t per = ceil_div(Lk, 64 * (int64_t)num_splits);
     return 64 * (per > 0 ? per : 1);
 }
 
@@ -168,9 +210,9 @@ attn_status attn_fwd_prefill(const attn_fwd_args *a, void *stream) {
     if (st != ATTN_OK) return st;
     if (a->B * a->Hq * a->Lq == 0) return ATTN_OK;
     FwdParams p = make_params(a);
+    if ((st = device_topology(p)) != ATTN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = (a->dtype == ATTN_BF16) ? attn::launch_prefill_bf16(p, s) : attn::launch_rows_f32(p, 0, s);
-    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return launch([&] { return a->dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, s) : attn::launch_rows_f32(p, 0, s); });
 }
 
 attn_status attn_fwd_decode_splitk(const attn_fwd_args *a, int32_t num_splits, float *o_part, float *m_part,
@@ -184,9 +226,9 @@ attn_status attn_fwd_decode_splitk(const attn_fwd_args *a, int32_t num_splits, f
     p.o_part = o_part;
     p.m_part = m_part;
     p.l_part = l_part;
+    if ((st = device_topology(p)) != ATTN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = (a->dtype == ATTN_BF16) ? attn::launch_decode_bf16(p, s) : attn::launch_rows_f32(p, 1, s);
-    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return launch([&] { return a->dtype == ATTN_BF16 ? attn::launch_decode_bf16(p, s) : attn::launch_rows_f32(p, 1, s); });
 }
 
 attn_status attn_fwd_prefill_splitk(const attn_fwd_args *a, int32_t num_splits, float *o_part, float *m_part,
@@ -208,15 +250,15 @@ attn_status attn_fwd_prefill_splitk(const attn_fwd_args *a, int32_t num_splits, 
     p.o_part = o_part;
     p.m_part = m_part;
     p.l_part = l_part;
-    hipError_t err = attn::launch_prefill_part_bf16(p, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    if ((st = device_topology(p)) != ATTN_OK) return st;
+    return launch([&] { return attn::launch_prefill_part_bf16(p, static_cast<hipStream_t>(stream)); });
 }
 
 int32_t attn_prefill_choose_splits(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int32_t cu_count) {
     if (B < 1 || Hq < 1 || Lq < 1 || Lk < 1) return 1;
     const int64_t cu = cu_count > 0 ? cu_count : 256;
-    const int64_t blocks = B * Hq * ((Lq + 127) / 128);
-    int64_t S = (kPrefillSplitSlots * cu + blocks - 1) / blocks;
+    const int64_t blocks = sat_mul(sat_mul(B, Hq), ceil_div(Lq, 128));
+    int64_t S = ceil_div(kPrefillSplitSlots * cu, blocks);
     const int64_t max_by_len = Lk / kPrefillSplitMinKeys;
     if (S > max_by_len) S = max_by_len;
     if (S > 65535) S = 65535;
@@ -232,9 +274,9 @@ attn_status attn_splitk_combine(const float *o_part, const float *m_part, const 
     if (!valid_dtype(o_dtype) || o_strides == nullptr) return ATTN_ERR_INVALID_ARG;
     for (int t = 0; t < 3; ++t)
         if (o_strides[t] < 0) return ATTN_ERR_INVALID_ARG;
-    const int64_t rows = B * Hq * Lq;
+    int64_t rows = 0;
     if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-    if (rows > kIntMax / 4) return ATTN_ERR_UNSUPPORTED;
+    if (!mul3(B, Hq, Lq, rows) || rows > kIntMax / 4) return ATTN_ERR_UNSUPPORTED;
     if (rows == 0) return ATTN_OK;
     if (o_part == nullptr || m_part == nullptr || l_part == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARG;
     if (!aligned(o_part, 4) || !aligned(m_part, 4) || !aligned(l_part, 4) || !aligned(o, (uintptr_t)elem_size(o_dtype)))
@@ -246,18 +288,17 @@ attn_status attn_splitk_combine(const float *o_part, const float *m_part, const 
     c.lse = lse;
     c.B = (int)B; c.Hq = (int)Hq; c.Lq = (int)Lq; c.D = (int)D; c.S = num_splits;
     c.o_bf16 = o_dtype == ATTN_BF16;
-    hipError_t err = attn::launch_combine(c, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return launch([&] { return attn::launch_combine(c, static_cast<hipStream_t>(stream)); });
 }
 
 int32_t attn_decode_choose_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int32_t cu_count) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Hq % Hkv != 0 || Lk <= 256) return 1;
     const int64_t cu = cu_count > 0 ? cu_count : 256;
-    const int64_t rblocks = ((Hq / Hkv) * Lq + 31) / 32;
-    const int64_t units = B * Hkv * rblocks;
+    const int64_t rblocks = (sat_mul(Hq / Hkv, Lq) - 1) / 32 + 1;
+    const int64_t units = sat_mul(sat_mul(B, Hkv), rblocks);
     const int64_t target = cu;                   // one workgroup per compute unit (the decode
                                                  // kernel's LDS stages hold one per CU at D = 128)
-    int64_t S = (target + units - 1) / units;
+    int64_t S = ceil_div(target, units);
     const int64_t max_by_len = Lk / 256;         // at least 256 keys per chunk
     if (S > max_by_len) S = max_by_len;
     if (S > 65535) S = 65535;
@@ -267,8 +308,12 @@ int32_t attn_decode_choose_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq
 
 size_t attn_decode_partial_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int32_t num_splits) {
     if (B < 0 || Hq < 0 || Lq < 0 || D < 0 || num_splits < 1) return 0;
-    const size_t rows = (size_t)B * (size_t)Hq * (size_t)Lq * (size_t)num_splits;
-    return rows * (size_t)D * sizeof(float) + 2 * rows * sizeof(float);
+    size_t rows, bytes;
+    if (__builtin_mul_overflow((size_t)B, (size_t)Hq, &rows) || __builtin_mul_overflow(rows, (size_t)Lq, &rows) ||
+        __builtin_mul_overflow(rows, (size_t)num_splits, &rows) ||
+        __builtin_mul_overflow(rows, ((size_t)D + 2) * sizeof(float), &bytes))
+        return 0;
+    return bytes;
 }
 
 int32_t attn_device_cu_count(int32_t device) {
@@ -284,13 +329,28 @@ int32_t attn_device_cu_count(int32_t device) {
     return v;
 }
 
+int32_t attn_device_xcd_count(int32_t device) {
+    static std::atomic<int32_t> cache[64];
+    if (device < 0) return -1;
+    if (device < 64) {
+        const int32_t c = cache[device].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, device) != hipSuccess) return -1;
+    if (v < 1) v = 1;
+    if (device < 64) cache[device].store(v, std::memory_order_relaxed);
+    return v;
+}
+
 size_t attn_fwd_args_size(void) { return sizeof(attn_fwd_args); }
 
 size_t attn_bwd_args_size(void) { return sizeof(attn_bwd_args); }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq) {
-    if (B < 0 || Hq < 0 || Lq < 0) return 0;
-    return 2 * bwd_rows_padded(B * Hq * Lq) * sizeof(float);
+    int64_t rows = 0;
+    if (B < 0 || Hq < 0 || Lq < 0 || !mul3(B, Hq, Lq, rows) || rows > INT64_MAX / 16) return 0;
+    return 2 * (size_t)bwd_rows_padded(rows) * sizeof(float);
 }
 
 attn_status attn_validate_bwd(const attn_bwd_args *a) {
@@ -398,8 +458,8 @@ attn_status attn_bwd(const attn_bwd_args *a, void *stream) {
     p.delta = a->workspace;
     p.lse_l2 = a->workspace + bwd_rows_padded(f->B * f->Hq * f->Lq);
     p.grad_bf16 = a->grad_dtype == ATTN_BF16;
-    hipError_t err = attn::launch_bwd_bf16(p, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    if ((st = device_topology(p.f)) != ATTN_OK) return st;
+    return launch([&] { return attn::launch_bwd_bf16(p, static_cast<hipStream_t>(stream)); });
 }
 
 const char *attn_status_str(attn_status s) {

@@ -93,8 +93,11 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
 // for them itself (wait_all_loads, or counted vmcnt waits).  With the
 // compiler's builtin, the compiler drains every load in flight before LDS
 // reads it cannot prove independent of the load's target, which serialises
-// loading and computing.  The assembly writes M0: no compiler-generated
-// instruction of a file that uses these may use M0.
+// loading and computing.  The assembly writes M0, which is not in the
+// clobber list: M0 is a reserved register, and the compiler neither tracks it
+// through inline assembly nor promises to restore it when listed.  So no
+// compiler-generated instruction of a file that uses these may touch M0; a
+// CPU test checks the generated code of every file that calls them.
 __device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc),
                  "s"(soff)
@@ -135,23 +138,23 @@ __device__ __forceinline__ int perm32(int r) {
 }
 
 // Work order for a grid of per-head tiles.  The dispatcher hands block b to XCD
-// b % 8; block b takes item (b % 8) * (n / 8) + b / 8 of a head-major list, so
-// each XCD runs a contiguous range of heads and a head's K/V stays in that XCD's
-// L2.  `rank` numbers a head's tiles, 0 first.  With `interleave` (tiles of
-// unequal cost, ranked heaviest first), windows of 4 heads, else 2, run their
-// tiles rank by rank across the window: with one head at a time the last head's
-// heaviest tiles start when the XCD is nearly drained and finish alone.
-// Windows are used only where they tile every XCD's range.
-constexpr int kXcds = 8;
+// b % X (X = the device's XCD count); block b takes item (b % X) * (n / X) +
+// b / X of a head-major list, so each XCD runs a contiguous range of heads and
+// a head's K/V stays in that XCD's L2.  `rank` numbers a head's tiles, 0
+// first.  With `interleave` (tiles of unequal cost, ranked heaviest first),
+// windows of 4 heads, else 2, run their tiles rank by rank across the window:
+// with one head at a time the last head's heaviest tiles start when the XCD
+// is nearly drained and finish alone.  Windows are used only where they tile
+// every XCD's range.
 struct WorkItem {
     int head;
     int rank;
 };
-__device__ __forceinline__ WorkItem xcd_work_item(int per_head, bool interleave) {
+__device__ __forceinline__ WorkItem xcd_work_item(int per_head, bool interleave, int nxcd) {
     const int n = (int)gridDim.x;
-    if (n % kXcds != 0) return {(int)blockIdx.x / per_head, (int)blockIdx.x % per_head};
-    const int per_xcd = n / kXcds;
-    const int item = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (nxcd < 1 || n % nxcd != 0) return {(int)blockIdx.x / per_head, (int)blockIdx.x % per_head};
+    const int per_xcd = n / nxcd;
+    const int item = (int)(blockIdx.x % nxcd) * per_xcd + (int)(blockIdx.x / nxcd);
     int win = 1;
     if (interleave) win = per_xcd % (4 * per_head) == 0 ? 4 : per_xcd % (2 * per_head) == 0 ? 2 : 1;
     const int span = win * per_head;

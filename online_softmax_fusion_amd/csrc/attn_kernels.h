@@ -43,6 +43,7 @@ struct FwdParams {
     float cap_inv;                      // 1 / cap_l2
     int window;                         // 1: apply win_left / win_right
     int win_left, win_right;            // keys left / right of the query position; < 0 = unbounded
+    int num_cus, num_xcds;              // compute units and XCDs of the launch device
 };
 
 // Visible key range [jmin, jmax] of the query at end-aligned position

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     // work item: XCD-contiguous ranges of heads; under a causal mask the last
     // query tile sees the most keys and goes first
     const int nqt = (p.Lq + BR - 1) / BR;
-    const WorkItem wi = xcd_work_item(nqt, p.causal && !p.window);
+    const WorkItem wi = xcd_work_item(nqt, p.causal && !p.window, p.num_xcds);
     const int bh = wi.head;
     const int qt = p.causal ? nqt - 1 - wi.rank : wi.rank;
     const int b = bh / p.Hq;
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
     // work item: XCD-contiguous ranges of K/V heads; key tiles in ascending
     // order (under the causal mask the first ones see the most rows)
     const int nkt = (p.Lk + BK - 1) / BK;
-    const WorkItem wi = xcd_work_item(nkt, p.causal && !p.window);
+    const WorkItem wi = xcd_work_item(nkt, p.causal && !p.window, p.num_xcds);
     const int bhk = wi.head;
     const int kt = wi.rank;
     const int b = bhk / p.Hkv;

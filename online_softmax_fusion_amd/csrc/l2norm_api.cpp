@@ -29,14 +29,16 @@ extern "C" {
 int64_t l2norm_max_onepass(int32_t x_dtype) { return kMaxOnepassVecs * 16 / elem_bytes(x_dtype); }
 
 size_t l2norm_workspace_bytes(int64_t rows, int32_t num_splits) {
-    if (rows <= 0 || num_splits <= 1) return 0;
-    return (size_t)rows * (size_t)num_splits * 8u;
+    size_t n;
+    if (rows <= 0 || num_splits <= 1 || __builtin_mul_overflow((size_t)rows, (size_t)num_splits * 8u, &n)) return 0;
+    return n;
 }
 
 int32_t l2norm_choose_splits(int64_t rows, int64_t H, int32_t x_dtype, int32_t cu_count) {
     if (rows <= 0 || H <= l2norm_max_onepass(x_dtype)) return 1;
     const int64_t cu = cu_count > 0 ? cu_count : 256;
-    int64_t S = (4 * cu + rows - 1) / rows;                  // four workgroups per compute unit
+    int64_t S = 4 * cu / rows + (4 * cu % rows != 0);        // four workgroups per compute unit
+    if (H > INT64_MAX / 4) H = INT64_MAX / 4;
     const int64_t max_by_len = H * elem_bytes(x_dtype) / 4096; // at least 4096 bytes per chunk
     if (S > max_by_len) S = max_by_len;
     if (S < 2) S = 2;                                       // the row does not fit one pass
@@ -49,6 +51,10 @@ attn_status l2norm_validate(const l2norm_args *a, int32_t num_splits) {
     if (a->rows < 0 || a->H < 0 || !valid_dtype(a->x_dtype)) return ATTN_ERR_INVALID_ARG;
     if (a->y != nullptr && !valid_dtype(a->y_dtype)) return ATTN_ERR_INVALID_ARG;
     if (num_splits < 1) return ATTN_ERR_INVALID_ARG;
+    // sizes the kernels hold (this also keeps the products below from overflowing)
+    if (a->rows > 0x7fffffff || a->H > ((int64_t)1 << 40) || a->x_stride > ((int64_t)1 << 40) ||
+        a->y_stride > ((int64_t)1 << 40))
+        return ATTN_ERR_UNSUPPORTED;
     if (a->x_stride < a->H || (a->y != nullptr && a->y_stride < a->H)) return ATTN_ERR_INVALID_ARG;
     if (a->rows > 0 && a->H > 0 && a->x == nullptr) return ATTN_ERR_INVALID_ARG;
     if (a->rows > 0 && a->y == nullptr && a->norm == nullptr) return ATTN_ERR_INVALID_ARG;   // nothing to write
@@ -94,6 +100,7 @@ attn_status l2norm_rows(const l2norm_args *a, int32_t num_splits, void *workspac
     p.S = num_splits;
     p.chunk_vecs = (int)chunk_vecs(a->H, a->x_dtype, num_splits);
     p.ws = workspace;
+    (void)hipGetLastError();   // report this call's launch error only
     const hipError_t err = attn::launch_l2norm(p, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

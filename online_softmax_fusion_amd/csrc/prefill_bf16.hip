@@ -263,7 +263,7 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     // work item: XCD-contiguous ranges of heads; under a causal mask the last
     // query tile sees the most keys and goes first
     const int nqt = (p.Lq + BR - 1) / BR;
-    const WorkItem wi = xcd_work_item(nqt, p.causal && !p.window);
+    const WorkItem wi = xcd_work_item(nqt, p.causal && !p.window, p.num_xcds);
     const int bh = wi.head;
     const int qt = p.causal ? nqt - 1 - wi.rank : wi.rank;
     const int b = bh / p.Hq;
@@ -525,14 +525,14 @@ hipError_t launch_prefill_t(const FwdParams &p, hipStream_t stream) {
 // (causal B1 H8 L8192: 0.192 vs 0.169 ms) unless rows see 8192 keys or more
 // (causal B1 H16 Lq 4096 Lk 16384: 0.466 vs 0.477 ms).
 int prefill_waves(const FwdParams &p) {
-    constexpr int64_t kCus = 256;
+    const int64_t cus = p.num_cus > 0 ? p.num_cus : 256;
     if (p.D != 128 || bias_cap(p.bias_kind) || p.window) return 4;   // the rule was measured at d = 128
     if (p.Lq < 1024) return 4;   // few rows: most waves of a 256-row tile would idle (Lq = 16: 678 vs 490 us)
     const int64_t avg_keys = p.causal ? (int64_t)p.Lk - ((int64_t)p.Lq - 1) / 2 : (int64_t)p.Lk;
     if (avg_keys < 4096) return 4;
     const int64_t blocks8 = (int64_t)p.B * p.Hq * (((int64_t)p.Lq + 255) / 256);
-    if (blocks8 < kCus) return 4;
-    if (p.causal && blocks8 < 2 * kCus && avg_keys < 8192) return 4;
+    if (blocks8 < cus) return 4;
+    if (p.causal && blocks8 < 2 * cus && avg_keys < 8192) return 4;
     return 8;
 }
 

@@ -1,9 +1,10 @@
 """Checks on the gfx950 code the compiler makes from the kernel sources (CPU
 only: hipcc cross-compiles, nothing runs).
 
-The decode and backward kernels issue their buffer-to-LDS loads from inline
-assembly that writes M0 itself; that is only sound while no compiler-generated
-instruction of those files reads or writes M0.  The kernels must also run
+Kernels that issue their buffer-to-LDS loads from inline assembly (the
+dma16 / dma4 helpers) write M0 themselves; that is only sound while no
+compiler-generated instruction of those files reads or writes M0, which is
+checked for every source that calls the helpers.  The kernels must also run
 without scratch (register spills) in every instantiation, and the dK/dV loop
 must not shuffle its accumulators between registers."""
 import os
@@ -44,8 +45,24 @@ def compiler_lines(asm):
             yield s
 
 
+def files_calling_lds_dma():
+    """Every kernel source that calls the inline-assembly buffer-to-LDS loads
+    (dma16 / dma4 of attn_device.h), which write M0 behind the compiler's back."""
+    out = []
+    for f in sorted(os.listdir(libbuild.CSRC)):
+        if f.endswith(".hip"):
+            with open(os.path.join(libbuild.CSRC, f)) as fh:
+                if re.search(r"\bdma(?:16|4)\(", fh.read()):
+                    out.append(f)
+    return out
+
+
+def test_lds_dma_users_found():
+    assert {"decode_bf16.hip", "bwd_bf16.hip"} <= set(files_calling_lds_dma())
+
+
 @needs_hipcc
-@pytest.mark.parametrize("src", ["decode_bf16.hip", "bwd_bf16.hip"])
+@pytest.mark.parametrize("src", files_calling_lds_dma())
 def test_m0_only_in_inline_asm(src, tmp_path):
     asm = device_asm(src, tmp_path)
     bad = [s for s in compiler_lines(asm) if re.search(r"\bm0\b", s)]

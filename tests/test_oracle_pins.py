@@ -33,6 +33,7 @@ The oracle is checked against things other than itself:
   are compiled and must fail these pins.
 """
 import json
+import functools
 import math
 import os
 import shutil
@@ -100,48 +101,51 @@ def assert_close(a, b, tol, what=""):
 
 
 # ----------------------------------------------------------------------------
-# Neptune notes section 3: the 2x4 example, three program shapes
+# Neptune notes section 3: the 2x4 example; what each program shape computes,
+# stated over whole rows (numpy), and the repair of section 4 as a merge
 # ----------------------------------------------------------------------------
 def three_loop(inp):
-    """max loop, then exp loop, then sum loop (three separate loops)."""
-    n, m = len(inp), len(inp[0])
-    xmax = [-math.inf] * n
-    for i in range(n):
-        for j in range(m):
-            xmax[i] = max(xmax[i], inp[i][j])
-    xexp = [[math.exp(inp[i][j] - xmax[i]) for j in range(m)] for i in range(n)]
-    xsum = [0.0] * n
-    for i in range(n):
-        for j in range(m):
-            xsum[i] += xexp[i][j]
-    return xmax, xsum
+    """Three separate passes: the row max, then sum_j exp(x_j - max)."""
+    x = np.asarray(inp, dtype=np.float64)
+    m = x.max(axis=1)
+    return m.tolist(), np.exp(x - m[:, None]).sum(axis=1).tolist()
 
 
 def naive_fused(inp):
-    """exp and sum moved into the max loop without any repair (wrong in general)."""
-    n, m = len(inp), len(inp[0])
-    xmax = [-math.inf] * n
-    xsum = [0.0] * n
-    for i in range(n):
-        for j in range(m):
-            xmax[i] = max(xmax[i], inp[i][j])
-            xsum[i] += math.exp(inp[i][j] - xmax[i])
-    return xmax, xsum
+    """Exponentials taken inside the max pass without repair: term j is
+    exp(x_j - max(x_0 .. x_j)), against the max seen so far, not the row's."""
+    x = np.asarray(inp, dtype=np.float64)
+    running = np.maximum.accumulate(x, axis=1)
+    return x.max(axis=1).tolist(), np.exp(x - running).sum(axis=1).tolist()
 
 
-def repaired_fused(inp):
-    """the fused loop keeping the previous and current max and repairing the sum
-    by exp(previous max - current max)."""
-    n, m = len(inp), len(inp[0])
-    xmax, xsum = [0.0] * n, [0.0] * n
-    for i in range(n):
-        prev, acc = -math.inf, 0.0
-        for j in range(m):
-            cur = max(prev, inp[i][j])
-            acc = math.exp(prev - cur) * acc + math.exp(inp[i][j] - cur)
-            prev = cur
-        xmax[i], xsum[i] = prev, acc
-    return xmax, xsum
+def merge(a, b):
+    """(m, s) states of two parts of a row combined with the repair function
+    h(t, r, r') = t exp(r - r') of section 4: both sums are moved to the
+    larger reference before they are added."""
+    (m1, s1), (m2, s2) = a, b
+    M = max(m1, m2)
+    if M == -math.inf:
+        return M, 0.0
+    return M, s1 * math.exp(m1 - M) + s2 * math.exp(m2 - M)
+
+
+def repaired_fused(inp, order="left"):
+    """The fused single pass: every element is the state (x_j, 1), and the
+    states are merged left to right ("left") or pairwise as a tree ("tree")."""
+    out_m, out_s = [], []
+    for row in inp:
+        states = [(float(v), 1.0) for v in row]
+        if order == "left":
+            st = functools.reduce(merge, states, (-math.inf, 0.0))
+        else:
+            while len(states) > 1:
+                states = [merge(states[i], states[i + 1]) if i + 1 < len(states) else states[i]
+                          for i in range(0, len(states), 2)]
+            st = states[0]
+        out_m.append(st[0])
+        out_s.append(st[1])
+    return out_m, out_s
 
 
 @pytest.fixture(scope="module")
@@ -181,9 +185,10 @@ def test_2x4_repaired_fusion_equals_three_loop(ex2x4):
 def test_2x4_repaired_fusion_random_rows():
     inp = RNG.standard_normal((2, 4)).tolist()
     _, s3 = three_loop(inp)
-    _, sr = repaired_fused(inp)
-    for a, b in zip(sr, s3):
-        assert abs(a - b) <= 1e-15 * b
+    for order in ("left", "tree"):
+        _, sr = repaired_fused(inp, order)
+        for a, b in zip(sr, s3):
+            assert abs(a - b) <= 1e-15 * b
 
 
 def test_oracle_reproduces_2x4_example(ex2x4):
@@ -233,18 +238,20 @@ def test_online_equals_two_pass(n):
 
 
 def test_printed_online_listing_is_garbled():
-    """The printed listing multiplies o by the already-updated l; that reading is
-    not the softmax-weighted sum, the corrected one is."""
-    x = [0.0, 1.0, 2.0]
-    vals = [1.0, 2.0, 3.0]
-    m, l, o = -math.inf, 0.0, 0.0
-    for xi, vi in zip(x, vals):
-        m_new = max(m, xi)
-        l = l * math.exp(m - m_new) + math.exp(xi - m_new)
-        o = o * l * math.exp(m - m_new) + math.exp(xi - m_new) * vi
-        m = m_new
+    """The CANN FlashAttention post's online-softmax listing (its online
+    softmax section) multiplies o by the already-updated l and returns o
+    without dividing by l.  Followed by hand on the scores x = (0, 1, 2) with
+    values (1, 2, 3) -- the max grows at every step, so every repair factor is
+    e^-1 -- it gives l = 1 + e^-1 + e^-2 and
+        o = 3 + e^-1 (2 + e^-1 + e^-2)(1 + e^-1 + e^-2) = 4.38428...,
+    while the softmax-weighted value is (1 + 2e + 3e^2) / (1 + e + e^2) =
+    2.5752...; the corrected recurrence (reading 10) gives the latter."""
+    e1, e2 = math.exp(-1.0), math.exp(-2.0)
+    printed = 3.0 + e1 * (2.0 + e1 + e2) * (1.0 + e1 + e2)
+    x, vals = [0.0, 1.0, 2.0], [1.0, 2.0, 3.0]
     good = softmax_standard_weighted(x, vals)
-    assert abs(o - good) > 0.1
+    assert abs(good - (1 + 2 * math.e + 3 * math.e ** 2) / (1 + math.e + math.e ** 2)) <= 1e-14
+    assert abs(printed - 4.3842822) <= 1e-6 and abs(printed - good) > 1.0
     assert abs(softmax_online_weighted(x, vals) - good) <= 1e-14
 
 

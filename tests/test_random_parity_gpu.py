@@ -1,13 +1,19 @@
 """Randomised parity sweep: the HIP path against the fp64 oracle over seeded
 random combinations of every option (GPU).
 
+Bars: those of the fixed cases (1e-5 for fp32 inputs; 1.5e-2 on O and 1e-3
+on LSE for bf16 inputs).  A bf16-stored O may also differ by half an ulp of
+the stored value, and every such case is run again with an fp32 O under the
+plain bar; a drawn softmax scale other than 1/sqrt(D) widens LSE (and fp32 O)
+by the score magnitude (compare()).
+
 Each case draws, from its own seed, the shapes (batch, heads, GQA ratio,
 ragged Lq and Lk, including Lq > Lk), head dimension, input and output dtypes,
 causal mask, bias kind (none, ALiBi, dense fp32 / bf16 with a broadcast
 batch), soft cap and sliding window, and for decode the split count and for
 the row L2 norm the row length, split count and output dtype.  The fixed
 cases of the other parity tests pin each option on its own; this sweep looks
-for interactions between them.  Tolerances are those of the fixed cases.
+for interactions between them.
 """
 import numpy as np
 import pytest
@@ -89,33 +95,28 @@ def make(c):
     return w, q, k, v, gkw, okw
 
 
-def compare(o, lse, O_ref, L_ref, dtype, what, c=None, vmax=None):
-    """The fixed cases' bars; where a drawn scale leaves their range, widened
-    O by the rounding of the stored output (half an ulp: 2^-8 |O| in bf16,
-    2^-24 |O| in fp32; the fixed bars assume |O| below ~3, which peaky rows
-    of a large scale exceed), and LSE -- and for fp32 inputs also O, whose
-    error is the weights' -- by the score magnitude |scale| sqrt(D) relative
-    to the default 1/sqrt(D) (fp32 dot products round in proportion to their
-    terms; with bf16 inputs the bf16 rounding of P dominates O).  Given
-    vmax = max |v|, a bf16 case may also use the worst-case rounding bound
-    2^-9 vmax + half an ulp of |O| (rows that see a few large values of v)."""
+def compare(o, lse, O_ref, L_ref, dtype, what, c=None):
+    """The fixed cases' bars (1e-5 on O and LSE for fp32 inputs; 1.5e-2 on O
+    and 1e-3 on LSE for bf16 inputs), with two allowances and no other:
+
+    * an O stored in bf16 may also differ by the rounding of that store, half
+      an ulp of the value (2^-8 |O|); the same call with an fp32 O is held to
+      the plain bar (every bf16-output case is re-run that way, see
+      check_both_outputs);
+    * a drawn softmax scale other than 1/sqrt(D) widens LSE, and for fp32
+      inputs also O, by |scale| sqrt(D) (the score magnitude relative to the
+      default scale): fp32 dot products round in proportion to their terms.
+    """
     o_tol, l_tol = TOL[dtype]
-    half_ulp = 0.0
     if c is not None and c.get("scale") is not None:
         mag = max(1.0, abs(c["scale"]) * c["D"] ** 0.5)
         l_tol *= mag
         if dtype == "f32":
             o_tol *= mag
-        half_ulp = 2.0 ** -8 if o.dtype == torch.bfloat16 else 2.0 ** -24
+    store = 2.0 ** -8 if o.dtype == torch.bfloat16 else 0.0
     og = o.float().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(og)), what + ": non-finite O"
-    tol = o_tol + half_ulp * np.abs(O_ref)
-    if vmax is not None and dtype == "bf16":
-        # the worst case of the rounding: P rounded to bf16 moves each weight
-        # by at most 2^-9 of itself, so O by at most 2^-9 max|v|, and the
-        # stored output adds half an ulp (2^-8 |O| in bf16, 2^-24 |O| in fp32)
-        store = 2.0 ** -8 if o.dtype == torch.bfloat16 else 2.0 ** -24
-        tol = np.maximum(tol, 2.0 ** -9 * vmax + store * np.abs(O_ref))
+    tol = o_tol + store * np.abs(O_ref)
     excess = np.abs(og - O_ref) - tol
     err_o = float(np.max(np.abs(og - O_ref))) if og.size else 0.0
     assert og.size == 0 or float(np.max(excess)) <= 0.0, "%s: O err %.3e" % (what, err_o)
@@ -124,6 +125,25 @@ def compare(o, lse, O_ref, L_ref, dtype, what, c=None, vmax=None):
     assert np.array_equal(np.isfinite(lg), fin) and np.all(lg[~fin] == -np.inf), what + ": LSE -inf pattern"
     err_l = float(np.max(np.abs(lg[fin] - L_ref[fin]))) if fin.any() else 0.0
     assert err_l <= l_tol, "%s: LSE err %.3e" % (what, err_l)
+    return err_o, err_l
+
+
+def check_both_outputs(run, c, O_ref, L_ref, what):
+    """run(out_dtype) -> (o, lse).  The drawn output type against the bars of
+    compare(); when that type is bf16, the same call with an fp32 O as well,
+    against the plain bar (no store allowance)."""
+    od = torch.float32 if c["out"] == "f32" else torch_dt(c["dtype"])
+    o, lse = run(od)
+    torch.cuda.synchronize()
+    compare(o, lse, O_ref, L_ref, c["dtype"], what, c)
+    if od == torch.bfloat16:
+        o32, lse32 = run(torch.float32)
+        torch.cuda.synchronize()
+        compare(o32, lse32, O_ref, L_ref, c["dtype"], what + " (fp32 O)", c)
+
+
+def torch_dt(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
 
 
 @pytest.mark.parametrize("i", range(N_PREFILL))
@@ -131,16 +151,13 @@ def test_random_prefill(i):
     c = draw_attention(6000 + i)
     print("random prefill", c, flush=True)
     w, q, k, v, gkw, okw = make(c)
-    od = torch.float32 if c["out"] == "f32" else None
-    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), c["causal"], out_dtype=od,
-                                   **gkw)
-    torch.cuda.synchronize()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), c["causal"], **okw)
-    compare(o, lse, O_ref, L_ref, c["dtype"], str(c), c, vmax=float(v.float().abs().max()))
+    check_both_outputs(lambda od: attn.attn_fwd_prefill(qc, kc, vc, w.softmax_scale(), c["causal"], out_dtype=od,
+                                                        **gkw), c, O_ref, L_ref, str(c))
     # the automatically planned forward gives the same result within the same bars
-    o2, lse2 = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), c["causal"], out_dtype=od, **gkw)
-    torch.cuda.synchronize()
-    compare(o2, lse2, O_ref, L_ref, c["dtype"], "attn_fwd " + str(c), c, vmax=float(v.float().abs().max()))
+    check_both_outputs(lambda od: attn.attn_fwd(qc, kc, vc, w.softmax_scale(), c["causal"], out_dtype=od, **gkw),
+                       c, O_ref, L_ref, "attn_fwd " + str(c))
 
 
 @pytest.mark.parametrize("i", range(N_LONG_PREFILL))
@@ -149,15 +166,27 @@ def test_random_long_prefill(i):
     c = draw_attention(6500 + i, long=True)
     print("random long prefill", c, flush=True)
     w, q, k, v, gkw, okw = make(c)
-    od = torch.float32 if c["out"] == "f32" else None
-    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), c["causal"], out_dtype=od,
-                                   **gkw)
-    torch.cuda.synchronize()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
     rng = np.random.default_rng(c["seed"])
     n = c["B"] * c["Hq"] * c["Lq"]
     rows = np.unique(np.concatenate([np.arange(0, 300), np.arange(n - 300, n), rng.integers(0, n, 200)]))
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), c["causal"], rows=rows, **okw)
-    compare(o.reshape(n, -1)[rows], lse.reshape(n)[rows], O_ref, L_ref, c["dtype"], str(c), c)
+
+    def run(od):
+        o, lse = attn.attn_fwd_prefill(qc, kc, vc, w.softmax_scale(), c["causal"], out_dtype=od, **gkw)
+        return o.reshape(n, -1)[rows], lse.reshape(n)[rows]
+
+    check_both_outputs(run, c, O_ref, L_ref, str(c))
+
+
+def draw_split_prefill(i):
+    c = draw_attention(9000 + i)
+    rng = np.random.default_rng(90000 + i)
+    c["dtype"] = "bf16"
+    c["out"] = "f32" if c["out"] == "f32" else "bf16"
+    c["Lk"] = int(rng.integers(1, 3000))
+    c["splits"] = int(rng.integers(1, 9))
+    return c
 
 
 @pytest.mark.parametrize("i", range(N_SPLIT_PREFILL))
@@ -165,21 +194,34 @@ def test_random_split_prefill(i):
     """The prefill kernel over key chunks and the combine (bf16 inputs), with
     1 to 8 chunks of whole 64-key tiles over up to 3000 keys (so chunks past
     the keys, and chunks a row cannot see, occur)."""
-    c = draw_attention(9000 + i)
-    rng = np.random.default_rng(90000 + i)
-    c["dtype"] = "bf16"
-    c["out"] = "f32" if c["out"] == "f32" else "bf16"
-    c["Lk"] = int(rng.integers(1, 3000))
-    c["splits"] = int(rng.integers(1, 9))
+    c = draw_split_prefill(i)
     print("random split prefill", c, flush=True)
     w, q, k, v, gkw, okw = make(c)
-    od = torch.float32 if c["out"] == "f32" else torch.bfloat16
     op, mp, lp = attn.attn_fwd_prefill_splitk(q.cuda(), k.cuda(), v.cuda(), c["splits"], w.softmax_scale(),
                                               c["causal"], **gkw)
-    o, lse = attn.attn_splitk_combine(op, mp, lp, out_dtype=od)
-    torch.cuda.synchronize()
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), c["causal"], **okw)
-    compare(o, lse, O_ref, L_ref, c["dtype"], str(c), c, vmax=float(v.float().abs().max()))
+    check_both_outputs(lambda od: attn.attn_splitk_combine(op, mp, lp, out_dtype=od), c, O_ref, L_ref, str(c))
+
+
+def test_regression_peaky_row_window_alibi():
+    """Split-prefill draw 1 (B1, Hq16/Hkv2, Lq102, Lk1133, window (93, 22),
+    ALiBi, bf16 O): one row at |O| = 3 came within 1.534e-2 of the oracle
+    with O stored in bf16, just past the plain bar, while its fp32 result was
+    within 9.9e-3.  The split prefill and the plain prefill are each held to
+    1.5e-2 with an fp32 O, and to 1.5e-2 + 2^-8 |O| (half an ulp of the
+    stored value) with a bf16 O."""
+    c = draw_split_prefill(1)
+    assert (c["B"], c["Hq"], c["Hkv"], c["Lq"], c["Lk"], c["window"], c["bias"]) == \
+        (1, 16, 2, 102, 1133, (93, 22), "alibi"), c
+    w, q, k, v, gkw, okw = make(c)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), c["causal"], **okw)
+    op, mp, lp = attn.attn_fwd_prefill_splitk(qc, kc, vc, c["splits"], w.softmax_scale(), c["causal"], **gkw)
+    c = dict(c, out="bf16")
+    check_both_outputs(lambda od: attn.attn_splitk_combine(op, mp, lp, out_dtype=od), c, O_ref, L_ref,
+                       "split prefill " + str(c))
+    check_both_outputs(lambda od: attn.attn_fwd_prefill(qc, kc, vc, w.softmax_scale(), c["causal"], out_dtype=od,
+                                                        **gkw), c, O_ref, L_ref, "prefill " + str(c))
 
 
 @pytest.mark.parametrize("i", range(N_DECODE))
@@ -187,12 +229,10 @@ def test_random_decode(i):
     c = draw_attention(7000 + i, decode=True)
     print("random decode", c, flush=True)
     w, q, k, v, gkw, okw = make(c)
-    od = torch.float32 if c["out"] == "f32" else q.dtype
-    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), c["splits"], w.softmax_scale(), c["causal"], out_dtype=od,
-                         **gkw)
-    torch.cuda.synchronize()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), c["causal"], **okw)
-    compare(o, lse, O_ref, L_ref, c["dtype"], str(c), c, vmax=float(v.float().abs().max()))
+    check_both_outputs(lambda od: attn.decode(qc, kc, vc, c["splits"], w.softmax_scale(), c["causal"],
+                                              out_dtype=od, **gkw), c, O_ref, L_ref, str(c))
 
 
 @pytest.mark.parametrize("i", range(N_BWD + N_LONG_BWD))
