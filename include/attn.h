@@ -259,6 +259,22 @@ attn_status attn_fwd_choose_plan(const attn_fwd_args *a, int32_t cu_count, attn_
  */
 attn_status attn_fwd(const attn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * attn_fwd_noalloc -- attn_fwd for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, hosts that forbid
+ * hipMalloc): the same plan, kernels and results as attn_fwd, with the
+ * split plans' partials in a fixed array that the library holds on each
+ * device (ATTN_NOALLOC_SCRATCH_BYTES per device, taken at the first call on
+ * that device and kept until the process ends).  Allocates nothing and takes
+ * no workspace.  A plan whose partials exceed the array (plan.workspace_bytes
+ * > ATTN_NOALLOC_SCRATCH_BYTES) returns ATTN_ERR_WORKSPACE and enqueues
+ * nothing; the prefill plan needs no array.  All calls on one device share
+ * its array: calls whose execution overlaps on one device (different streams
+ * without ordering between them) race on it; calls on one stream are ordered.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+attn_status attn_fwd_noalloc(const attn_fwd_args *a, void *stream);
+
 /* attn_decode_partial_bytes -- bytes of o_part + m_part + l_part for a decode call. */
 size_t attn_decode_partial_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int32_t num_splits);
 

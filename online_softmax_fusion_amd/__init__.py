@@ -147,6 +147,8 @@ def load_library():
     lib.attn_fwd_choose_plan.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [P, vp, ctypes.c_size_t, vp]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_noalloc.argtypes = [P, vp]
+    lib.attn_fwd_noalloc.restype = ctypes.c_int
     PB = ctypes.POINTER(AttnBwdArgs)
     lib.attn_bwd.argtypes = [PB, vp]
     lib.attn_bwd.restype = ctypes.c_int
@@ -575,6 +577,31 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bi
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
     return out, lse
+
+
+def attn_fwd_noalloc(q, k, v, scale: Optional[float] = None, causal: bool = False, *, bias=None,
+                     alibi_slopes=None, out=None, lse=None, softcap: float = 0.0,
+                     window: Optional[Tuple[int, int]] = None):
+    """``attn_fwd`` without a workspace: the split plans keep their partials in
+    the library's fixed per-device array.  ``out`` (and ``lse``, if wanted) must be
+    given, so that the call itself allocates nothing; returns them."""
+    lib = load_library()
+    _check_4d("q", q)
+    B, Hq, Lq, D = q.shape
+    if out is None:
+        raise ValueError("attn_fwd_noalloc: out must be given")
+    _check_out("out", out, (B, Hq, Lq, D), q.device)
+    if lse is not None:
+        _check_lse(lse, B * Hq * Lq, q.device)
+    a = _make_args(q, k, v, scale, causal, bias, alibi_slopes, out, lse, softcap, window)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_noalloc(ctypes.byref(a), _stream(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_noalloc")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def l2norm_max_onepass(dtype: torch.dtype = torch.bfloat16) -> int:

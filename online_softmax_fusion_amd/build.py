@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn_mi355x.so")
 SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "bwd_bf16.hip", "rows_f32.hip", "combine.hip", "l2norm.hip",
-           "attn_api.cpp", "l2norm_api.cpp"]
+           "noalloc.hip", "attn_api.cpp", "l2norm_api.cpp"]
 # per-source device flags: the decode kernel keeps its matrix-core results in
 # ordinary VGPRs (its LDS use leaves one workgroup per CU, and the compiler's
 # default then moves the accumulators to AGPRs and back on every loop trip)
