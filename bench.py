@@ -5,9 +5,21 @@ Default run (N = 1):
     is one attn_fwd_prefill call over inputs already resident in HBM.  `value`
     is its throughput in algorithmic TFLOP/s (4 * d FLOP per visible
     query/key pair, masked pairs not counted).
+  * the other prefill workloads, under "prefill_legs", each with its own
+    roofline: ALiBi causal B=2, H=16, L=8192 (slopes formed in registers); the
+    same problem with the ALiBi values given as a bf16 [H, L, L] bias tensor
+    broadcast over the batch (bound by HBM: the bias bytes of the visible
+    pairs are read once per batch element); the long causal B=1, H=8, L=32768.
   * decode leg -- the split-K GQA workload B=16, Hq=32, Hkv=8, Lk=32768,
     d=128, 32 chunks of 1024 keys; one step is the local split-K kernel
     followed by the combine.  Reported under "decode" in algorithmic GB/s.
+    The batch-1 decode (B=1, H=8, Lk=32768, split count chosen for the
+    device) is reported the same way under "decode_b1"; its K/V copies are
+    rotated so that each step reads from HBM, not from the 256 MB cache.
+  * run metadata -- per leg the kernel's mean / p10 / p50 / p90 launch time
+    and the graphics clock read from the driver's metrics while the leg ran
+    ("sclk"); the GPU, its compute-unit and XCD counts and the host CPU model
+    under "machine".  `--legs` runs a subset (for profiling runs).
   * roofline -- for the dominant kernel of each leg, algorithmic work per
     launch / the average launch duration measured with HIP events on the
     stream the kernel runs on.
@@ -154,8 +166,8 @@ def measured_traffic(kernel: str, workload: str, sources) -> "int | None":
             table = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = table.get(kernel)
-    if not ent or ent.get("workload") != workload or ent.get("source_digest") != source_digest(sources):
+    ent = table.get("%s @ %s" % (kernel, workload))
+    if not ent or ent.get("source_digest") != source_digest(sources):
         return None
     return int(ent["traffic_bytes"])
 
@@ -169,6 +181,122 @@ def _sum_traffic(parts):
             return None
         total += t
     return total
+
+
+# ----------------------------------------------------------------------------
+# run metadata: GPU clock while a leg runs, host CPU model, percentiles
+# ----------------------------------------------------------------------------
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _stats_ms(durs):
+    """mean and percentiles of sorted per-launch durations (ms)."""
+    n = len(durs)
+    return {"mean": round(sum(durs) / n, 4), "p10": round(durs[n // 10], 4), "p50": round(durs[n // 2], 4),
+            "p90": round(durs[(9 * n) // 10], 4)}
+
+
+class ClockSampler:
+    """The GPU's graphics clock while a leg runs: a background thread reads the
+    driver's metrics table (amdsmi gpu_metrics, current clock of each XCD) every
+    few milliseconds between start() and stop(), and stop() reports the median
+    over the samples of the mean over XCDs.  The device is found by its PCI
+    address.  Reports None (with the reason) where the metrics cannot be read;
+    it never touches the GPU's settings."""
+
+    _handle = None
+    _why = None
+    _lock = None
+
+    def __init__(self, period_s=0.005):
+        import threading
+
+        self.period = period_s
+        self.samples = []
+        self.avg_samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        if ClockSampler._lock is None:
+            ClockSampler._lock = threading.Lock()
+
+    @classmethod
+    def _open(cls):
+        with cls._lock:
+            if cls._handle is not None or cls._why is not None:
+                return cls._handle
+            try:
+                import torch
+                import amdsmi
+
+                props = torch.cuda.get_device_properties(torch.cuda.current_device())
+                want = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0), props.pci_bus_id,
+                                           props.pci_device_id)
+                amdsmi.amdsmi_init()
+                handles = amdsmi.amdsmi_get_processor_handles()
+                match = [h for h in handles if str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower().startswith(want)]
+                if len(match) == 1:
+                    cls._handle = match[0]
+                elif len(handles) == 1:
+                    cls._handle = handles[0]
+                else:
+                    cls._why = "no metrics device at PCI address %s" % want
+            except Exception as e:   # metrics are optional: report why they are missing
+                cls._why = "%s: %s" % (type(e).__name__, e)
+            return cls._handle
+
+    @staticmethod
+    def _read(h):
+        import amdsmi
+
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        vals = [v for v in (m.get("current_gfxclks") or []) if isinstance(v, int) and 0 < v < 10000]
+        if not vals and isinstance(m.get("current_gfxclk"), int):
+            vals = [m["current_gfxclk"]]
+        avg = m.get("average_gfxclk_frequency")
+        return (sum(vals) / len(vals) if vals else None), (avg if isinstance(avg, int) and 0 < avg < 10000 else None)
+
+    def _run(self):
+        h = self._open()
+        while h is not None and not self._stop.is_set():
+            try:
+                v, avg = self._read(h)
+            except Exception:
+                v = avg = None
+            if v is not None:
+                self.samples.append(v)
+            if avg is not None:
+                self.avg_samples.append(avg)
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=2.0)
+        if not self.samples:
+            return {"mhz": None, "samples": 0, "why": ClockSampler._why or "no samples"}
+        x = sorted(self.samples)
+        a = sorted(self.avg_samples)
+        return {"mhz": round(x[len(x) // 2], 1), "min": round(x[0], 1), "max": round(x[-1], 1),
+                "average_gfxclk_mhz": a[len(a) // 2] if a else None,
+                "samples": len(x), "source": "amdsmi gpu_metrics current_gfxclks, mean over XCDs, "
+                                             "median over the leg's warm-up and timed steps (the driver "
+                                             "refreshes the table about once a second)"}
 
 
 # ----------------------------------------------------------------------------
@@ -201,9 +329,13 @@ def time_prefill(w, steps, warmup, warm_s=1.0):
     kw = {"softcap": w.softcap, "window": w.window}
     if w.bias == "alibi":
         kw["alibi_slopes"] = synth.alibi_slopes(w.Hq).cuda()
+    elif w.bias == "dense":
+        kw["bias"] = synth.alibi_bias_tensor(w, "bf16", "cuda")   # [Hq, Lq, Lk], broadcast over B
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
     scale = w.softmax_scale()
+    torch.cuda.synchronize()
+    clock = ClockSampler().start()
     n = warm_up(lambda i: attn.attn_fwd_prefill(q, k, v, scale, w.causal, out=o, lse=lse, **kw), warmup, warm_s)
     log("prefill: %d untimed warm-up steps" % n)
     stream = torch.cuda.current_stream()
@@ -216,14 +348,15 @@ def time_prefill(w, steps, warmup, warm_s=1.0):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = clock.stop()
     durs = sorted(a.elapsed_time(b) for a, b in ev)
     avg_ms = sum(durs) / len(durs)
     flops = attention_flops(w.B, w.Hq, w.Lq, w.Lk, w.D, w.causal, w.window)
-    log("prefill: wall %.3f ms/step, kernel avg %.4f ms (p10 %.4f, p90 %.4f)" %
-        (wall * 1e3 / steps, avg_ms, durs[len(durs) // 10], durs[(9 * len(durs)) // 10]))
-    del q, k, v, o, lse
+    log("prefill: wall %.3f ms/step, kernel avg %.4f ms (p10 %.4f, p90 %.4f), sclk %s MHz" %
+        (wall * 1e3 / steps, avg_ms, durs[len(durs) // 10], durs[(9 * len(durs)) // 10], sclk.get("mhz")))
+    del q, k, v, o, lse, kw
     torch.cuda.empty_cache()
-    return wall / steps, avg_ms * 1e-3, flops, durs
+    return {"step_s": wall / steps, "kern_s": avg_ms * 1e-3, "flops": flops, "durs": durs, "sclk": sclk}
 
 
 def time_decode(w, steps, warmup, warm_s=1.0):
@@ -257,6 +390,8 @@ def time_decode(w, steps, warmup, warm_s=1.0):
             evs[1].record(torch.cuda.current_stream())
         attn.attn_splitk_combine(op, mp, lp, out=o, lse=lse)
 
+    torch.cuda.synchronize()
+    clock = ClockSampler().start()
     n = warm_up(step, warmup, warm_s)
     log("decode: %d untimed warm-up steps" % n)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -265,13 +400,15 @@ def time_decode(w, steps, warmup, warm_s=1.0):
         step(i, ev[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    sclk = clock.stop()
     durs = sorted(a.elapsed_time(b) for a, b in ev)
     avg_ms = sum(durs) / len(durs)
 
-    log("decode: S=%d, step %.4f ms, partial kernel avg %.4f ms" % (S, wall * 1e3, avg_ms))
+    log("decode: %s S=%d, step %.4f ms, partial kernel avg %.4f ms (p10 %.4f, p90 %.4f)" %
+        (w.name, S, wall * 1e3, avg_ms, durs[len(durs) // 10], durs[(9 * len(durs)) // 10]))
     del q, k, v, kvs, op, mp, lp, o, lse
     torch.cuda.empty_cache()
-    return wall, avg_ms * 1e-3, S
+    return {"step_s": wall, "kern_s": avg_ms * 1e-3, "S": S, "durs": durs, "sclk": sclk, "copies": copies}
 
 
 def time_backward(w, steps, warmup, warm_s=1.0):
@@ -501,7 +638,7 @@ def cpu_baseline(w, budget_s=15.0):
     if n > 1:
         t1, f1 = run(n)
     log("cpu baseline: %d head(s) in %.2f s on %d threads" % (n, t1, threads))
-    return {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "%d whole K/V head(s) with their %d query head(s) each (%d query rows x %d keys%s, "
                       "d=%d), drawn with the workload's recipe, of %s; fp64; %.1f s" %
                       (n, G, w.Lq, w.Lk, ", causal" if w.causal else "", w.D, w.name, t1)}
@@ -509,15 +646,17 @@ def cpu_baseline(w, budget_s=15.0):
 
 def _counter_kib(csv_path, counter, kernel_substr, grid=None):
     """Mean value of `counter` (KiB) over the dispatches whose kernel name
-    contains `kernel_substr` (and, if given, whose grid has `grid` work-items:
+    contains `kernel_substr` (a string, or a tuple of strings that must all
+    appear) (and, if given, whose grid has `grid` work-items:
     the bench launches some kernels on more than one shape) in a rocprofv3
     counter_collection.csv."""
     import csv
 
+    parts = (kernel_substr,) if isinstance(kernel_substr, str) else tuple(kernel_substr)
     vals = []
     with open(csv_path) as f:
         for row in csv.DictReader(f):
-            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"] and \
+            if row["Counter_Name"] == counter and all(x in row["Kernel_Name"] for x in parts) and \
                     (grid is None or int(row["Grid_Size"]) == grid):
                 vals.append(float(row["Counter_Value"]))
     if not vals:
@@ -526,11 +665,15 @@ def _counter_kib(csv_path, counter, kernel_substr, grid=None):
 
 
 def traffic_table(d):
-    """HBM bytes per launch of the two kernels timed by a default bench run,
-    from FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same
-    counters read for a plain device copy of known size."""
+    """HBM bytes per launch of the kernels a default bench run times, from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same
+    counters read for a plain device copy of known size.  Under `d`: fetch/
+    and write/ (a default bench run), fetch_b1/ and write_b1/ (a run of the
+    decode_b1 leg alone, whose decode grid the plan leg shares), cfetch/ and
+    cwrite/ (the copy)."""
     import glob
     import synth
+    import online_softmax_fusion_amd as attn
 
     def csv_of(sub):
         hits = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
@@ -545,50 +688,120 @@ def traffic_table(d):
     out = {"_about": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per "
                      "dispatch, mean over the dispatches of the run), each scaled by the factor that makes the "
                      "same counter read the known size of a plain 1 GiB device copy (bench.py "
-                     "--copy-calibration). source_digest ties an entry to the kernel source it was measured on "
-                     "(comments and whitespace aside); "
+                     "--copy-calibration). Keys are 'kernel @ workload'. source_digest ties an entry to the "
+                     "kernel source it was measured on (comments and whitespace aside); "
                      "bench.py reports null traffic once that source changes.",
            "calibration": {"copy_bytes": copy_bytes, "fetch_kib_per_copy": cf, "write_kib_per_copy": cw,
                            "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5)}}
     wp, wd, wbk, wl, wll = synth.C2_CAUSAL, synth.C4_DECODE, synth.BWD_PREFILL, synth.L2N_ROWS, synth.L2N_LONG
+    w3, w3d, w5, w5d = synth.C3_ALIBI, synth.C3_DENSE, synth.C5_PREFILL, synth.C5_DECODE
     S = wd.splits
+    S5 = attn.attn_decode_choose_splits(w5d.B, w5d.Hq, w5d.Hkv, w5d.Lq, w5d.Lk, 256)
     Sl = 128                                        # l2norm_choose_splits for the long rows on 256 CUs
     q_e = wbk.B * wbk.Hq * wbk.Lq * wbk.D * 2           # one [B, Hq, L, D] bf16 tensor
     kv_e = wbk.B * wbk.Hkv * wbk.Lk * wbk.D * 2
     rows4 = wbk.B * wbk.Hq * wbk.Lq * 4                # one fp32 value per query row
+
+    def pf(w):
+        return prefill_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D)
+
+    def pgrid(w):   # 64 work-items per 32 query rows, whatever the wave count
+        return (w.Lq // 32) * 64 * w.B * w.Hq
+
     entries = [
-        # kernel, workload, sources, algorithmic bytes, grid work-items of that workload's launch
-        # (the prefill entry names its 4-wave form: the backward leg's non-causal forward runs the
-        # 8-wave form on the same grid)
-        ("prefill_bf16_kernel<128, 4,", wp, PREFILL_SOURCES, prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.Lq, wp.Lk, wp.D),
-         (wp.Lq // 128) * wp.B * wp.Hq * 256),
-        ("decode_bf16_kernel", wd, DECODE_SOURCES,
-         decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S), S * wd.B * wd.Hkv * 256),
+        # kernel, name match, workload, sources, algorithmic bytes, grid work-items, counter runs
+        # (the C2 entry names its 4-wave form: the backward leg's non-causal forward runs the
+        # 8-wave form on the same grid; the template's third argument is the score modifier:
+        # 0 none, 1 ALiBi, 3 dense bf16 bias)
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 4, 0, true>",), wp, PREFILL_SOURCES, pf(wp), pgrid(wp),
+         ""),
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 1, true>"), w3, PREFILL_SOURCES, pf(w3), pgrid(w3),
+         ""),
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 3, true>"), w3d, PREFILL_SOURCES,
+         pf(w3d) + dense_bias_bytes(w3d), pgrid(w3d), ""),
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 0, true>"), w5, PREFILL_SOURCES, pf(w5), pgrid(w5),
+         ""),
+        ("decode_bf16_kernel", ("decode_bf16_kernel",), wd, DECODE_SOURCES,
+         decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S), S * wd.B * wd.Hkv * 256, ""),
+        ("decode_bf16_kernel", ("decode_bf16_kernel",), w5d, DECODE_SOURCES,
+         decode_partial_kernel_bytes(w5d.B, w5d.Hq, w5d.Hkv, w5d.Lq, w5d.Lk, w5d.D, S5), None, "_b1"),
         # dQ: reads Q, dO, O, LSE, K, V; writes dQ, Delta, LSE*log2(e)
-        ("bwd_dq_kernel", wbk, BWD_SOURCES, 4 * q_e + rows4 + 2 * kv_e + 2 * rows4,
-         (wbk.Lq // 128) * wbk.B * wbk.Hq * 256),
+        ("bwd_dq_kernel", ("bwd_dq_kernel",), wbk, BWD_SOURCES, 4 * q_e + rows4 + 2 * kv_e + 2 * rows4,
+         (wbk.Lq // 128) * wbk.B * wbk.Hq * 256, ""),
         # dK/dV: reads Q, dO, Delta, LSE*log2(e), K, V; writes dK, dV
-        ("bwd_dkdv_kernel", wbk, BWD_SOURCES, 2 * q_e + 2 * rows4 + 4 * kv_e, (wbk.Lk // 128) * wbk.B * wbk.Hkv * 256),
-        ("l2norm_onepass_kernel", wl, L2NORM_SOURCES, l2norm_bytes(wl.rows, wl.H, 2, 2), (wl.rows // 4) * 256),
+        ("bwd_dkdv_kernel", ("bwd_dkdv_kernel",), wbk, BWD_SOURCES, 2 * q_e + 2 * rows4 + 4 * kv_e,
+         (wbk.Lk // 128) * wbk.B * wbk.Hkv * 256, ""),
+        ("l2norm_onepass_kernel", ("l2norm_onepass_kernel",), wl, L2NORM_SOURCES, l2norm_bytes(wl.rows, wl.H, 2, 2),
+         (wl.rows // 4) * 256, ""),
         # split path: the partial kernel reads x and writes one partial per chunk; the scale kernel
         # reads the partials and x and writes y and the norms
-        ("l2norm_partial_kernel", wll, L2NORM_SOURCES, wll.rows * wll.H * 4 + wll.rows * Sl * 8, wll.rows * Sl * 256),
-        ("l2norm_scale_kernel", wll, L2NORM_SOURCES, wll.rows * wll.H * 8 + wll.rows * Sl * 8 + wll.rows * 4,
-         wll.rows * Sl * 256),
+        ("l2norm_partial_kernel", ("l2norm_partial_kernel",), wll, L2NORM_SOURCES,
+         wll.rows * wll.H * 4 + wll.rows * Sl * 8, wll.rows * Sl * 256, ""),
+        ("l2norm_scale_kernel", ("l2norm_scale_kernel",), wll, L2NORM_SOURCES,
+         wll.rows * wll.H * 8 + wll.rows * Sl * 8 + wll.rows * 4, wll.rows * Sl * 256, ""),
     ]
-    for match, w, srcs, alg, grid in entries:
-        kernel = match.split("<")[0]
+    for kernel, match, w, srcs, alg, grid, run in entries:
         try:
-            fk = _counter_kib(csv_of("fetch"), "FETCH_SIZE", match, grid)
-            wk = _counter_kib(csv_of("write"), "WRITE_SIZE", match, grid)
-        except ValueError:
+            fk = _counter_kib(csv_of("fetch" + run), "FETCH_SIZE", match, grid)
+            wk = _counter_kib(csv_of("write" + run), "WRITE_SIZE", match, grid)
+        except (ValueError, FileNotFoundError):
             continue
         fb, wbytes = int(round(fk * 1024 * fscale)), int(round(wk * 1024 * wscale))
-        out[kernel] = {"workload": w.name, "grid_work_items": grid, "source_digest": source_digest(srcs),
-                       "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
-                       "fetch_bytes": fb, "write_bytes": wbytes, "traffic_bytes": fb + wbytes,
-                       "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wbytes) / alg, 4)}
+        out["%s @ %s" % (kernel, w.name)] = {
+            "kernel": kernel, "workload": w.name, "grid_work_items": grid, "source_digest": source_digest(srcs),
+            "fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "fetch_bytes": fb, "write_bytes": wbytes,
+            "traffic_bytes": fb + wbytes, "algorithmic_bytes": alg,
+            "traffic_over_algorithmic": round((fb + wbytes) / alg, 4)}
     return out
+
+
+ALL_LEGS = ("prefill", "prefill_c3", "prefill_c3_dense", "prefill_c5", "decode", "decode_b1", "plan", "l2norm",
+            "backward")
+
+
+def dense_bias_bytes(w, elem=2) -> int:
+    """bias elements of the visible pairs, read once per (batch, head) pass."""
+    return w.B * w.Hq * visible_pairs(w.Lq, w.Lk, w.causal, w.window) * elem
+
+
+def prefill_leg_json(w, r):
+    """One prefill leg: whole-step throughput, kernel percentiles, and the
+    roofline of prefill_bf16_kernel (matrix-core bound; with a dense bias the
+    bias bytes make it bound by HBM, and both fractions are given)."""
+    flops = r["flops"]
+    kern_tf = flops / r["kern_s"] / 1e12
+    leg = {"workload": w.name, "bias": w.bias, "value": round(flops / r["step_s"] / 1e12, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(r["step_s"] * 1e3, 4), "kernel_ms": _stats_ms(r["durs"]), "sclk": r["sclk"]}
+    traffic = measured_traffic("prefill_bf16_kernel", w.name, PREFILL_SOURCES)
+    if w.bias == "dense":
+        nbytes = prefill_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D) + dense_bias_bytes(w)
+        gbs = nbytes / r["kern_s"] / 1e9
+        leg["roofline"] = {"kernel": "prefill_bf16_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "traffic": traffic, "algorithmic_bytes": nbytes,
+                           "mfma_achieved_tflops": round(kern_tf, 2),
+                           "mfma_frac": round(kern_tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        leg["roofline"] = {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": round(kern_tf, 2),
+                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(kern_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    return leg
+
+
+def decode_leg_json(w, r):
+    """One decode leg: the whole step (local split-K step + combine) in
+    algorithmic GB/s, and the roofline of the local step's kernel."""
+    S = r["S"]
+    d_bytes = decode_step_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, S)
+    k_bytes = decode_partial_kernel_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, S)
+    gbs = d_bytes / r["step_s"] / 1e9
+    kgbs = k_bytes / r["kern_s"] / 1e9
+    return {"workload": w.name, "splits": S, "kv_copies_rotated": r["copies"], "value": round(gbs, 1),
+            "unit": "GB/s", "ms_per_step": round(r["step_s"] * 1e3, 4), "kernel_ms": _stats_ms(r["durs"]),
+            "sclk": r["sclk"],
+            "roofline": {"kernel": "decode_bf16_kernel", "bound": "hbm", "achieved": round(kgbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_bf16_kernel", w.name, DECODE_SOURCES)}}
 
 
 def main():
@@ -603,6 +816,9 @@ def main():
     ap.add_argument("--splits", type=int, default=None, help="override the decode split count")
     ap.add_argument("--backward", default=None,
                     help="backward workload name (default: non-causal B4 H32 L4096), or 'none' to skip")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated subset of %s (default: all; the headline needs 'prefill')" %
+                         ",".join(ALL_LEGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--plan-sweep", choices=("causal", "noncausal"), default=None,
                     help="only time both forward paths over the planner's shape grid (JSON lines)")
@@ -648,54 +864,53 @@ def main():
     wd = synth.WORKLOADS[args.decode] if args.decode else synth.C4_DECODE
     if args.splits:
         wd = wd.with_(splits=args.splits)
+    legs = set(ALL_LEGS if args.legs == "all" else args.legs.split(","))
+    unknown = legs - set(ALL_LEGS)
+    if unknown:
+        sys.exit("unknown legs: %s (known: %s)" % (",".join(sorted(unknown)), ",".join(ALL_LEGS)))
+    if args.backward == "none":
+        legs.discard("backward")
+    wb = synth.WORKLOADS[args.backward] if args.backward not in (None, "none") else synth.BWD_PREFILL
 
     torch.cuda.synchronize()
-    step_s, kern_s, flops, _ = time_prefill(wp, args.steps, args.warmup, args.warm_seconds)
-    d_step_s, d_kern_s, S = time_decode(wd, args.steps, args.warmup, args.warm_seconds)
-    plan_res = time_plan(synth.PLAN_SHORT_GQA)
-    plan_long_res = time_plan(synth.PLAN_LONG_KEYS)
-    l2_res = [time_l2norm(w, args.steps, args.warmup, args.warm_seconds) for w in (synth.L2N_ROWS, synth.L2N_LONG)]
-    wb = None if args.backward == "none" else synth.WORKLOADS[args.backward or synth.BWD_PREFILL.name]
-    if wb is not None:
-        b_step_s, b_kern_s, b_flops = time_backward(wb, args.steps, args.warmup, args.warm_seconds)
-
-    p_tflops = flops / step_s / 1e12
-    p_kern_tflops = flops / kern_s / 1e12
-    d_bytes = decode_step_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S)
-    d_kern_bytes = decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S)
-    d_gbs = d_bytes / d_step_s / 1e9
-    d_kern_gbs = d_kern_bytes / d_kern_s / 1e9
-
     result = {
-        "metric": METRIC,
-        "value": round(p_tflops, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 inputs)",
+        "metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 inputs)",
         "config": {"workload": wp.name, "B": wp.B, "H": wp.Hq, "Lq": wp.Lq, "Lk": wp.Lk, "D": wp.D,
                    "causal": wp.causal, "bias": wp.bias, "softcap": wp.softcap,
                    "window": list(wp.window) if wp.window else None, "parallelism": "single GPU"},
-        "roofline": {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": round(p_kern_tflops, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(p_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_bf16_kernel", wp.name, PREFILL_SOURCES)},
-        "decode": {"workload": wd.name, "splits": S, "value": round(d_gbs, 1), "unit": "GB/s",
-                   "ms_per_step": round(d_step_s * 1e3, 4),
-                   "roofline": {"kernel": "decode_bf16_kernel", "bound": "hbm", "achieved": round(d_kern_gbs, 1),
-                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_kern_gbs / HBM_PEAK_GBS, 4),
-                                "traffic": measured_traffic("decode_bf16_kernel", wd.name, DECODE_SOURCES)}},
     }
-    result["plan"] = plan_res
-    result["plan_long_keys"] = plan_long_res
-    result["l2norm"] = l2_res
-    if wb is not None:
+    props = torch.cuda.get_device_properties(0)
+    result["machine"] = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+                         "compute_units": attn.attn_device_cu_count(0), "xcds": attn.attn_device_xcd_count(0),
+                         "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
+    if "prefill" in legs:
+        r = time_prefill(wp, args.steps, args.warmup, args.warm_seconds)
+        leg = prefill_leg_json(wp, r)
+        result["value"] = leg["value"]
+        result["ms_per_step"] = leg["ms_per_step"]
+        result["roofline"] = leg["roofline"]
+        result["kernel_ms"] = leg["kernel_ms"]
+        result["sclk"] = leg["sclk"]
+    extra = [("prefill_c3", synth.C3_ALIBI), ("prefill_c3_dense", synth.C3_DENSE), ("prefill_c5", synth.C5_PREFILL)]
+    pl = [prefill_leg_json(w, time_prefill(w, args.steps, args.warmup, args.warm_seconds))
+          for name, w in extra if name in legs]
+    if pl:
+        result["prefill_legs"] = pl
+    if "decode" in legs:
+        result["decode"] = decode_leg_json(wd, time_decode(wd, args.steps, args.warmup, args.warm_seconds))
+    if "decode_b1" in legs:
+        result["decode_b1"] = decode_leg_json(synth.C5_DECODE, time_decode(synth.C5_DECODE, args.steps, args.warmup,
+                                                                           args.warm_seconds))
+    if "plan" in legs:
+        result["plan"] = time_plan(synth.PLAN_SHORT_GQA)
+        result["plan_long_keys"] = time_plan(synth.PLAN_LONG_KEYS)
+    if "l2norm" in legs:
+        result["l2norm"] = [time_l2norm(w, args.steps, args.warmup, args.warm_seconds)
+                            for w in (synth.L2N_ROWS, synth.L2N_LONG)]
+    if "backward" in legs:
+        b_step_s, b_kern_s, b_flops = time_backward(wb, args.steps, args.warmup, args.warm_seconds)
         b_kern_tflops = b_flops / b_kern_s / 1e12
         result["backward"] = {
             "workload": wb.name, "causal": wb.causal, "value": round(b_flops / b_step_s / 1e12, 2),
@@ -705,7 +920,7 @@ def main():
                          "frac": round(b_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": _sum_traffic([("bwd_dq_kernel", wb.name, BWD_SOURCES),
                                                   ("bwd_dkdv_kernel", wb.name, BWD_SOURCES)])}}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and "prefill" in legs:
         result["cpu_baseline"] = cpu_baseline(wp, args.cpu_budget)
     else:
         result["cpu_baseline"] = None

@@ -73,6 +73,14 @@ C5_PREFILL = Workload("long-causal-prefill-bf16-B1-H8-L32768-d128", 1, 8, 8, 327
 C5_DECODE = Workload("long-decode-bf16-B1-H8-Lk32768-d128", 1, 8, 8, 1, 32768, 128,
                      "bf16", False, "none", 1005)
 
+# Config 3 with its bias given as a tensor: the same ALiBi values stored as a
+# bf16 [Hq, Lq, Lk] tensor and broadcast over the batch (the dense-bias form of
+# the interface), so that the bias is read from memory instead of being formed
+# in registers.  Under the causal mask half of its 2 GiB is read per batch
+# element.
+C3_DENSE = Workload("dense-bias-causal-prefill-bf16-B2-H16-L8192-d128", 2, 16, 16, 8192, 8192, 128,
+                    "bf16", True, "dense", 1003)
+
 # The next score modifiers (SoftCap and Window of the Neptune notes, section 9),
 # on shapes of the workloads above: a Gemma-style cap of 50 on the causal
 # B4 H32 L4096 prefill, and a causal sliding window of 4096 keys (the query's
@@ -100,7 +108,7 @@ PLAN_SHORT_GQA = Workload("short-gqa-bf16-B1-Hq32-Hkv8-Lq16-Lk32768-d128", 1, 32
 PLAN_LONG_KEYS = Workload("long-keys-prefill-bf16-B1-H8-Lq2048-Lk32768-d128", 1, 8, 8, 2048, 32768, 128,
                           "bf16", True, "none", 1013)
 
-WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C4_DECODE, C5_PREFILL, C5_DECODE,
+WORKLOADS = {w.name: w for w in (C1_TINY, C2_CAUSAL, C3_ALIBI, C3_DENSE, C4_DECODE, C5_PREFILL, C5_DECODE,
                                  SOFTCAP_PREFILL, WINDOW_PREFILL, BWD_PREFILL, PLAN_SHORT_GQA, PLAN_LONG_KEYS)}
 
 
@@ -154,6 +162,22 @@ def alibi_slopes(H: int) -> torch.Tensor:
     """slope_h = 2^(-8 (h+1) / H) for h = 0..H-1, as fp32 (CPU)."""
     h = torch.arange(H, dtype=torch.float64)
     return torch.pow(2.0, -8.0 * (h + 1.0) / H).to(torch.float32)
+
+
+def alibi_bias_tensor(w: Workload, dtype: str = "bf16", device="cpu") -> torch.Tensor:
+    """The ALiBi bias of the workload written out as a tensor [Hq, Lq, Lk]:
+    -slope_h * |(i + Lk - Lq) - j| (query positions aligned to the end of the
+    keys), formed in fp32 from the fp32 slopes and stored in ``dtype``.  An
+    input, like the slopes: both the kernels and the oracle read the stored
+    values."""
+    sl = alibi_slopes(w.Hq).to(device)
+    qpos = torch.arange(w.Lq, device=device, dtype=torch.float32) + float(w.Lk - w.Lq)
+    kpos = torch.arange(w.Lk, device=device, dtype=torch.float32)
+    dist = (qpos[:, None] - kpos[None, :]).abs_()
+    out = torch.empty((w.Hq, w.Lq, w.Lk), dtype=torch_dtype(dtype), device=device)
+    for h in range(w.Hq):
+        out[h] = (dist * -sl[h]).to(out.dtype)
+    return out
 
 
 def make_qkv(w: Workload, device="cpu"):

@@ -105,3 +105,32 @@ def test_source_digest_ignores_comments_only():
     assert bench.code_text(src) != bench.code_text(src.replace("a = 1", "a = 2"))
     assert "// kept" in bench.code_text(src)
     assert bench.code_text("x = '/'; /* c */ y") == "x = '/'; y"
+
+
+def test_dense_bias_bytes():
+    """bf16 bias of the visible pairs, once per (batch, head): for the dense-bias
+    ALiBi workload (B=2, H=16, L=8192, causal) that is 2*16*L(L+1)/2 elements,
+    i.e. twice the ~1.07 GB that one batch element reads."""
+    w = synth.C3_DENSE
+    L = w.Lq
+    assert bench.dense_bias_bytes(w) == w.B * w.Hq * (L * (L + 1) // 2) * 2
+    per_batch = bench.dense_bias_bytes(w) // w.B
+    assert abs(per_batch - 1.07e9) / 1.07e9 < 0.01
+
+
+def test_stats_ms_percentiles():
+    d = sorted(float(x) for x in range(1, 21))     # 1 .. 20
+    s = bench._stats_ms(d)
+    assert s == {"mean": 10.5, "p10": 3.0, "p50": 11.0, "p90": 19.0}
+
+
+def test_alibi_bias_tensor_matches_slopes():
+    """The dense form of the ALiBi workload holds -slope_h * |i + Lk - Lq - j|."""
+    w = synth.C3_DENSE.with_(Hq=3, Lq=5, Lk=9)
+    b = synth.alibi_bias_tensor(w, "f32")
+    sl = synth.alibi_slopes(3).double()
+    for h in range(3):
+        for i in range(5):
+            for j in range(9):
+                want = -float(sl[h]) * abs(i + 4 - j)
+                assert abs(float(b[h, i, j]) - want) <= 1e-6 * max(1.0, abs(want))

@@ -30,8 +30,10 @@ def sample_rows(L, rng, n=10):
     return sorted({r for r in fixed + rnd if 0 <= r < L})
 
 
-def check_heads(w, q, k, v, o, lse, heads, rows, slopes=None):
-    """Compare rows of heads [(b, h), ...] against the oracle, per head."""
+def check_heads(w, q, k, v, o, lse, heads, rows, slopes=None, bias=None):
+    """Compare rows of heads [(b, h), ...] against the oracle, per head
+    (rows=None: every row of the head).  ``bias``: a dense [Hq, Lq, Lk] bias
+    on the GPU, broadcast over the batch."""
     G = w.Hq // w.Hkv
     worst_o = worst_l = 0.0
     for b, h in heads:
@@ -42,9 +44,13 @@ def check_heads(w, q, k, v, o, lse, heads, rows, slopes=None):
         kw = {}
         if slopes is not None:
             kw["alibi_slopes"] = slopes[h:h + 1]
+        if bias is not None:
+            kw["bias"] = bias[h:h + 1].float().cpu()
         O_ref, L_ref = oracle.attention(qh, kh, vh, w.softmax_scale(), w.causal, rows=rows, **kw)
-        og = o[b, h, rows].float().cpu().numpy()
-        lg = lse[b, h, rows].cpu().numpy()
+        sel = slice(None) if rows is None else rows
+        og = o[b, h, sel].float().cpu().numpy()
+        lg = lse[b, h, sel].cpu().numpy()
+        O_ref, L_ref = O_ref.reshape(og.shape), L_ref.reshape(lg.shape)
         eo = float(np.max(np.abs(og - O_ref)))
         el = float(np.max(np.abs(lg - L_ref)))
         assert eo <= O_TOL, "%s b=%d h=%d: O err %.3e" % (w.name, b, h, eo)
@@ -66,6 +72,38 @@ def test_prefill_fullsize_sampled(w):
     heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2)} |
                    {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(2)})
     check_heads(w, q, k, v, o, lse, heads, sample_rows(w.Lq, rng), slopes)
+
+
+@pytest.mark.parametrize("w", [synth.C2_CAUSAL, synth.C3_ALIBI], ids=lambda w: w.name)
+def test_prefill_fullsize_whole_heads(w):
+    """Two heads of the full-size launch compared in full: every row and
+    every column of O and every LSE, against the oracle over the whole head."""
+    print("full-size prefill, whole heads", w.name, flush=True)
+    q, k, v = synth.make_qkv(w, device="cuda")
+    slopes = synth.alibi_slopes(w.Hq) if w.bias == "alibi" else None
+    kw = {"alibi_slopes": slopes.cuda()} if slopes is not None else {}
+    o, lse = attn.attn_fwd_prefill(q, k, v, w.softmax_scale(), w.causal, **kw)
+    torch.cuda.synchronize()
+    check_heads(w, q, k, v, o, lse, [(0, 0), (w.B - 1, w.Hq - 1)], None, slopes)
+
+
+def test_prefill_fullsize_dense_bias():
+    """The ALiBi causal workload with its bias given as a bf16 [H, L, L]
+    tensor broadcast over the batch (the form bench.py times): sampled rows of
+    five heads, and one head in full, against the oracle on the same stored
+    bias values."""
+    w = synth.C3_DENSE
+    print("full-size prefill, dense bias", w.name, flush=True)
+    rng = np.random.default_rng(w.seed + 1)
+    q, k, v = synth.make_qkv(w, device="cuda")
+    bias = synth.alibi_bias_tensor(w, "bf16", "cuda")
+    o, lse = attn.attn_fwd_prefill(q, k, v, w.softmax_scale(), w.causal, bias=bias)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2)} |
+                   {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(2)})
+    check_heads(w, q, k, v, o, lse, heads, sample_rows(w.Lq, rng), bias=bias)
+    check_heads(w, q, k, v, o, lse, [(1, 3)], None, bias=bias)
 
 
 @pytest.mark.parametrize("w", [synth.C4_DECODE, synth.C5_DECODE], ids=lambda w: w.name)
