@@ -262,19 +262,30 @@ class ClockSampler:
         if not vals and isinstance(m.get("current_gfxclk"), int):
             vals = [m["current_gfxclk"]]
         avg = m.get("average_gfxclk_frequency")
-        return (sum(vals) / len(vals) if vals else None), (avg if isinstance(avg, int) and 0 < avg < 10000 else None)
+        stamp = m.get("firmware_timestamp")
+        if not isinstance(stamp, int):
+            stamp = m.get("system_clock_counter")
+        return ((sum(vals) / len(vals) if vals else None), (avg if isinstance(avg, int) and 0 < avg < 10000 else None),
+                stamp if isinstance(stamp, int) else None)
 
     def _run(self):
+        # only tables the firmware wrote after the leg started count: the
+        # driver refreshes them about once a second, so the first reads can
+        # still describe the time before the leg
         h = self._open()
+        first = None
         while h is not None and not self._stop.is_set():
             try:
-                v, avg = self._read(h)
+                v, avg, stamp = self._read(h)
             except Exception:
-                v = avg = None
-            if v is not None:
-                self.samples.append(v)
-            if avg is not None:
-                self.avg_samples.append(avg)
+                v = avg = stamp = None
+            if first is None:
+                first = stamp if stamp is not None else -1
+            elif stamp is None or stamp != first:
+                if v is not None:
+                    self.samples.append(v)
+                if avg is not None:
+                    self.avg_samples.append(avg)
             self._stop.wait(self.period)
 
     def start(self):
@@ -289,14 +300,15 @@ class ClockSampler:
         if self._thread is not None:
             self._thread.join(timeout=2.0)
         if not self.samples:
-            return {"mhz": None, "samples": 0, "why": ClockSampler._why or "no samples"}
+            return {"mhz": None, "samples": 0,
+                    "why": ClockSampler._why or "the metrics table was not refreshed while the leg ran"}
         x = sorted(self.samples)
         a = sorted(self.avg_samples)
         return {"mhz": round(x[len(x) // 2], 1), "min": round(x[0], 1), "max": round(x[-1], 1),
                 "average_gfxclk_mhz": a[len(a) // 2] if a else None,
-                "samples": len(x), "source": "amdsmi gpu_metrics current_gfxclks, mean over XCDs, "
-                                             "median over the leg's warm-up and timed steps (the driver "
-                                             "refreshes the table about once a second)"}
+                "samples": len(x), "source": "amdsmi gpu_metrics current_gfxclks, mean over XCDs, median "
+                                             "over the tables written while the leg's warm-up and timed "
+                                             "steps ran"}
 
 
 # ----------------------------------------------------------------------------
@@ -809,7 +821,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--warm-seconds", type=float, default=1.0,
+    ap.add_argument("--warm-seconds", type=float, default=2.0,
                     help="keep warming up (untimed) until this much time has passed")
     ap.add_argument("--prefill", default=None, help="prefill workload name (default: causal B4 H32 L4096)")
     ap.add_argument("--decode", default=None, help="decode workload name (default: GQA B16 Lk32768)")

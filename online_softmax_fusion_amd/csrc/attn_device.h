@@ -87,8 +87,10 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
     return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-// Buffer-to-LDS loads: 16 (or 4) bytes per lane from buffer offset voff + soff
-// into LDS at m0 + 16 * lane (4 * lane).  Inline assembly, so that the
+// Buffer-to-LDS loads: 16 (or 4) bytes per lane from buffer offset voff into
+// LDS at m0 + 16 * lane (4 * lane).  The whole offset is the vector offset,
+// which the hardware checks against the descriptor's range (loads past it
+// read zero); a scalar offset would not be checked.  Inline assembly, so that the
 // compiler's wait insertion does not see them: a kernel that uses them waits
 // for them itself (wait_all_loads, or counted vmcnt waits).  With the
 // compiler's builtin, the compiler drains every load in flight before LDS
@@ -98,9 +100,8 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
 // through inline assembly nor promises to restore it when listed.  So no
 // compiler-generated instruction of a file that uses these may touch M0; a
 // CPU test checks the generated code of every file that calls them.
-__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc),
-                 "s"(soff)
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t m0, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
                  : "memory");
 }
 __device__ __forceinline__ void dma4(const i32x4 &rsrc, uint32_t m0, uint32_t voff) {

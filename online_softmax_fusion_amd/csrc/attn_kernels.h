@@ -9,13 +9,17 @@ namespace attn {
 
 // kBiasNoneScaled: no bias, score formed explicitly (used when the scale is not
 // positive).  The *Cap kinds add the soft cap of the scaled score.
+// kBiasDenseBf16Tiled: a bf16 dense bias whose rows are contiguous and
+// 16-byte aligned, loaded a tile at a time into LDS beside K and V (chosen by
+// the prefill launcher; never set by the host interface).
 enum BiasKind {
     kBiasNone = 0, kBiasAlibi = 1, kBiasDenseF32 = 2, kBiasDenseBf16 = 3, kBiasNoneScaled = 4,
-    kBiasNoneCap = 5, kBiasAlibiCap = 6, kBiasDenseF32Cap = 7, kBiasDenseBf16Cap = 8
+    kBiasNoneCap = 5, kBiasAlibiCap = 6, kBiasDenseF32Cap = 7, kBiasDenseBf16Cap = 8,
+    kBiasDenseBf16Tiled = 9
 };
-// the bias part of a kind, and whether it carries the soft cap
-constexpr int bias_base(int kind) { return kind == kBiasNoneCap ? kBiasNoneScaled : kind >= kBiasAlibiCap ? kind - 5 : kind; }
-constexpr bool bias_cap(int kind) { return kind >= kBiasNoneCap; }
+// whether a kind carries the soft cap, and its bias part
+constexpr bool bias_cap(int kind) { return kind >= kBiasNoneCap && kind <= kBiasDenseBf16Cap; }
+constexpr int bias_base(int kind) { return kind == kBiasNoneCap ? kBiasNoneScaled : bias_cap(kind) ? kind - 5 : kind; }
 
 // One attention problem after validation.  Strides are in elements.
 struct FwdParams {
@@ -44,6 +48,7 @@ struct FwdParams {
     int window;                         // 1: apply win_left / win_right
     int win_left, win_right;            // keys left / right of the query position; < 0 = unbounded
     int num_cus, num_xcds;              // compute units and XCDs of the launch device
+    uint32_t bias_plane_bytes;          // kBiasDenseBf16Tiled: bytes of one (b, h) plane of the bias
 };
 
 // Visible key range [jmin, jmax] of the query at end-aligned position

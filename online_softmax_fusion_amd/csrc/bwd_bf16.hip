@@ -145,7 +145,9 @@ __device__ __forceinline__ void store4(void *base, int64_t idx, bool bf16, float
 // A 64-row tile (rows `src` .. + 63, `lbytes` apart, `nvalid` of them present)
 // into the LDS tile at byte address `lds`: lane fills LDS bytes
 // [i*T*16 + wave*1024 + 16*lane, +16) of round i from byte offset goff of the
-// source (+ round i's rows, RROWS rows per round).  Missing rows read as 0.
+// source (+ round i's rows, RROWS rows per round).  Missing rows read as 0:
+// the whole offset goes in the vector offset, which the hardware checks
+// against the descriptor's range (the scalar offset is not checked).
 template <int D, int T>
 __device__ __forceinline__ void dma_tile(const void *src, uint32_t lbytes, int nvalid, uint32_t lds, int wave,
                                          uint32_t goff) {
@@ -156,7 +158,7 @@ __device__ __forceinline__ void dma_tile(const void *src, uint32_t lbytes, int n
     static_assert(RROWS % 16 == 0, "rounds must keep the swizzle");
     const i32x4 rs = rsrc_words(src, (uint32_t)(nvalid - 1) * lbytes + D * 2);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) dma16(rs, lds + i * T * 16 + wave * 1024, goff, (uint32_t)(i * RROWS) * lbytes);
+    for (int i = 0; i < NC; ++i) dma16(rs, lds + i * T * 16 + wave * 1024, goff + (uint32_t)(i * RROWS) * lbytes);
 }
 
 // this lane's source offset inside a tile: LDS position wave*1024 + 16*lane

@@ -174,9 +174,9 @@ __device__ __forceinline__ void issue_block(const FwdParams &p, const uint16_t *
     const i32x4 rv = rsrc_words(vp + (int64_t)kb0 * p.v_sl, (uint32_t)(nvalid - 1) * vl_bytes + D * 2);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < C::NL; ++i) dma16(rk, dst + i * 1024, koff[i], 0u);
+    for (int i = 0; i < C::NL; ++i) dma16(rk, dst + i * 1024, koff[i]);
 #pragma unroll
-    for (int i = 0; i < C::NL; ++i) dma16(rv, dst + C::TB + i * 1024, voff[i], 0u);
+    for (int i = 0; i < C::NL; ++i) dma16(rv, dst + C::TB + i * 1024, voff[i]);
 }
 
 template <int D, int NW, int NST, int BIAS>

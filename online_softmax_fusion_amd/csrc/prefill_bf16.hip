@@ -73,8 +73,13 @@ struct TileCfg {
 // lk / lv: LDS tiles; this lane's K operand chunk for k-step ks is at byte
 // kbase ^ (ks << 5) (+32 rows per key block), its transposing-read word for
 // d-block db at vbase ^ (db << 6) (+ key rows).
+// Byte offset in an LDS bias tile of 16-byte chunk c (keys 8c .. 8c+7 of the
+// tile) of row R: chunks are XOR-swizzled by the row so that the 16 rows read
+// by 16 lanes at once hit 16 different bank groups.
+__device__ __forceinline__ int bias_lds_off(int R, int c) { return (R * 8 + (c ^ ((R >> 1) & 7))) * 16; }
+
 template <int D, int BIAS, bool MASK>
-__device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk, const char *lv,
+__device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk, const char *lv, const char *lb,
                                              int kbase, int vbase,
                                              const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32],
                                              float &m_run, float &l_run, int kt0, int qrow, int qpos,
@@ -109,6 +114,19 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     }
     // 2. score modifier; tile max (raw scores when the scale is folded)
     const float sc = p.scale_log2;
+    // tiled dense bias: this lane's values come 8 consecutive keys (one
+    // 16-byte chunk of its row) at a time; element e of block kb is key
+    // 32 kb + 16 (e / 8) + 8 hh + e % 8 of the tile, in chunk 4 kb + 2 (e / 8) + hh
+    // chunk c of the lane's row R sits at bias_lds_off(R, c) = bbase ^ (c << 4),
+    // bbase = bias_lds_off(R, 0); bbase is made opaque here so that the four
+    // chunk addresses are formed per tile instead of being held in registers
+    // across the loop
+    int bbase = 0;
+    if constexpr (BK == kBiasDenseBf16Tiled) {
+        bbase = bias_lds_off(((int)threadIdx.x >> 6) * 32 + (lane & 31), 0);
+        asm volatile("" : "+v"(bbase));
+    }
+    u32x4 bch{};
     // ALiBi distance qpos - j = dbase - (a compile-time offset of the element)
     const float dbase = (float)(qpos - kt0 - hh * 8);
     float mx = -INFINITY;
@@ -117,12 +135,18 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int j = kt0 + kb * 32 + (e >> 3) * 16 + hh * 8 + (e & 7);
+            if (BK == kBiasDenseBf16Tiled && (e & 7) == 0)
+                bch = load16(lb + (bbase ^ ((4 * kb + 2 * (e >> 3) + hh) << 4)));
             float x = s[kb][e];
             if (!FOLD) {
                 x *= sc;
                 if (CAP) x = soft_cap(x, p.cap_l2, p.cap_k, p.cap_inv);   // in log2 units
                 if (BK == kBiasAlibi) {
                     x = fmaf(-slope_l2, fabsf(dbase - (float)(kb * 32 + (e >> 3) * 16 + (e & 7))), x);
+                } else if (BK == kBiasDenseBf16Tiled) {
+                    const uint32_t wv = bch[(e & 7) >> 1];
+                    const float bv = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+                    x = fmaf(bv, kLog2e, x);
                 } else if (BK == kBiasDenseF32 || BK == kBiasDenseBf16) {
                     const int bi = min(qrow, p.Lq - 1);
                     const int bj = min(j, p.Lk - 1);
@@ -205,26 +229,36 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
 // diagonal of every row of the workgroup and inside the keys.  On masked
 // tiles a wave whose rows are all above the tile's keys skips the work.
 template <int D, int BIAS, bool MASK>
-__device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, const char *lv,
+__device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, const char *lv, const char *lb,
                                           int kbase, int vbase,
                                           const u32x4 (&qreg)[D / 16], f32x16 (&oacc)[D / 32], float &m_run,
                                           float &l_run, int kt0, int wrow0, int wjmin, int wjmax, int qrow, int qpos,
                                           int jmin, int jmax, float slope_l2, int b, int h, int lane) {
     if (MASK && !((wrow0 < p.Lq) && kt0 <= wjmax && kt0 + TileCfg<D>::BC - 1 >= wjmin)) return;
-    process_tile<D, BIAS, MASK>(p, lk, lv, kbase, vbase, qreg, oacc, m_run, l_run, kt0, qrow, qpos, jmin, jmax,
+    process_tile<D, BIAS, MASK>(p, lk, lv, lb, kbase, vbase, qreg, oacc, m_run, l_run, kt0, qrow, qpos, jmin, jmax,
                                 slope_l2, b, h, lane);
 }
 
 // Direct global->LDS loads of K/V tile T_ into the LDS tile arrays KOFF_ /
-// VOFF_: lane
+// VOFF_ (and, with a tiled bias, of the workgroup's rows of bias columns
+// [64 T_, 64 T_ + 64) into BOFF_): lane
 // fills LDS bytes [i*T*16 + wave*1024 + 16*lane, +16) of each tile from the
-// byte offsets kgoff[i] / vgoff[i] inside the tile.  Rows past the end of K/V
-// fall outside the descriptor's range and read as zero (with overlapping rows
-// they read valid data, which the mask discards).  A macro, because the
+// byte offsets kgoff / vgoff (+ round i's rows) inside the tile.  The whole
+// offset goes in the vector offset, which the hardware checks against the
+// descriptor's range (the scalar offset is not checked), so rows past the end
+// of K/V read as zero (with overlapping rows they read valid data, which the
+// mask discards).  A macro, because the
 // buffer-to-LDS builtins have to appear in the kernel body itself.
-#define ATTN_ISSUE_TILE_LOADS(T_, KOFF_, VOFF_)                                                                 \
+#define ATTN_ISSUE_TILE_LOADS(T_, KOFF_, VOFF_, BOFF_)                                                          \
     do {                                                                                                        \
         const int j0_ = (T_) * BC;                                                                              \
+        if constexpr (TB) {                                                                                     \
+            _Pragma("unroll") for (int i_ = 0; i_ < NB; ++i_) {                                                 \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                       \
+                    rb, (__attribute__((address_space(3))) void *)((BOFF_) + i_ * T * 16 + wave * 1024), 16,     \
+                    (int)(bgoff + (uint32_t)i_ * bround + (uint32_t)j0_ * 2u), 0, 0, 0);                       \
+            }                                                                                                   \
+        }                                                                                                       \
         const int nvalid_ = min(BC, p.Lk - j0_);                                                                \
         const __amdgpu_buffer_rsrc_t rk_ =                                                                      \
             make_rsrc(kp + (int64_t)j0_ * p.k_sl, (uint32_t)(nvalid_ - 1) * kl_bytes + D * 2);                  \
@@ -233,10 +267,10 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, const char *lk, co
         _Pragma("unroll") for (int i_ = 0; i_ < NC; ++i_) {                                                     \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
                 rk_, (__attribute__((address_space(3))) void *)((KOFF_) + i_ * T * 16 + wave * 1024), 16,        \
-                (int)kgoff, (int)(i_ * RROWS * kl_bytes), 0, 0);                                                                            \
+                (int)(kgoff + (uint32_t)(i_ * RROWS) * kl_bytes), 0, 0, 0);                                     \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                           \
                 rv_, (__attribute__((address_space(3))) void *)((VOFF_) + i_ * T * 16 + wave * 1024), 16,        \
-                (int)vgoff, (int)(i_ * RROWS * vl_bytes), 0, 0);                                                                            \
+                (int)(vgoff + (uint32_t)(i_ * RROWS) * vl_bytes), 0, 0, 0);                                     \
         }                                                                                                       \
     } while (0)
 
@@ -259,6 +293,13 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     __shared__ __attribute__((aligned(1024))) char lds_k1[C::TILE];
     __shared__ __attribute__((aligned(1024))) char lds_v0[C::TILE];
     __shared__ __attribute__((aligned(1024))) char lds_v1[C::TILE];
+    // tiled dense bias: the workgroup's BR rows x 64 keys of bf16 per tile
+    constexpr bool TB = (BIAS == kBiasDenseBf16Tiled);
+    constexpr int BTILE = TB ? BR * BC * 2 : 16;
+    constexpr int NB = BTILE / (T * 16);     // 16-byte direct loads per thread per bias tile
+    static_assert(!TB || NB * T * 16 == BTILE, "bias tile does not split evenly");
+    __shared__ __attribute__((aligned(TB ? 1024 : 16))) char lds_b0[BTILE];
+    __shared__ __attribute__((aligned(TB ? 1024 : 16))) char lds_b1[BTILE];
 
     // work item: XCD-contiguous ranges of heads; under a causal mask the last
     // query tile sees the most keys and goes first
@@ -349,6 +390,23 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
         kgoff = (uint32_t)key * kl_bytes + (uint32_t)((pc ^ C::swz_k(row)) * 16);
         vgoff = (uint32_t)row * vl_bytes + (uint32_t)((pc ^ C::swz_v(row)) * 16);
     }
+    // tiled bias: round i fills slot s = i*T + tid of the tile (row s / 8,
+    // position s % 8), which holds chunk (s % 8) ^ swizzle(row) of that row.
+    // Rounds are T / 8 rows apart (a multiple of 16, so the swizzle is the
+    // same in every round).  Rows past the last query and keys past the
+    // plane's end lie outside the descriptor's range and read as zero (those
+    // rows' results are not stored; keys past Lk are masked).
+    static_assert(!TB || (T / 8) % 16 == 0, "bias rounds must keep the swizzle");
+    const __amdgpu_buffer_rsrc_t rb =
+        TB ? make_rsrc(static_cast<const uint16_t *>(p.bias) + (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh,
+                       p.bias_plane_bytes)
+           : make_rsrc(p.k, 0u);
+    const uint32_t bround = TB ? (uint32_t)(T / 8) * (uint32_t)p.bias_si * 2u : 0u;   // bytes between rounds
+    uint32_t bgoff = 0;
+    if constexpr (TB) {
+        const int R = q0 + (tid >> 3);
+        bgoff = (uint32_t)R * (uint32_t)p.bias_si * 2u + (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) * 16);
+    }
 
     f32x16 oacc[C::DB];
 #pragma unroll
@@ -360,7 +418,7 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
 
 
     if (t_end > t_first) {
-        ATTN_ISSUE_TILE_LOADS(t_first, lds_k0, lds_v0);
+        ATTN_ISSUE_TILE_LOADS(t_first, lds_k0, lds_v0, lds_b0);
         wait_vmem();
         __syncthreads();
     }
@@ -370,7 +428,8 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     // step; the unmasked middle runs two tiles per trip so that each LDS
     // buffer's address is a constant.
 #define ATTN_STEP(MASK_, BUF_, T_)                                                                               \
-    tile_step<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, kbase, vbase, qreg, oacc,    \
+    tile_step<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, (BUF_) ? lds_b1 : lds_b0,   \
+                              kbase, vbase, qreg, oacc,                                                         \
                               m_run, l_run, (T_) * BC, wrow0, wjmin, wjmax, qrow, qpos, jmin, jmax, slope_l2, b, h, \
                               lane)
 #define ATTN_GENERIC_STEP(T_)                                                                                   \
@@ -378,13 +437,13 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
         const int tg_ = (T_);                                                                                   \
         const bool masked_ = tg_ < u_first || tg_ >= u_end;                                                     \
         if (((tg_ - t_first) & 1) == 0) {                                                                       \
-            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k1, lds_v1);                                \
+            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k1, lds_v1, lds_b1);                                \
             if (masked_)                                                                                        \
                 ATTN_STEP(true, 0, tg_);                                                                        \
             else                                                                                                \
                 ATTN_STEP(false, 0, tg_);                                                                       \
         } else {                                                                                                \
-            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k0, lds_v0);                                \
+            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k0, lds_v0, lds_b0);                                \
             if (masked_)                                                                                        \
                 ATTN_STEP(true, 1, tg_);                                                                        \
             else                                                                                                \
@@ -396,11 +455,11 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     int t = t_first;
     for (; t < t_end && !(t >= u_first && ((t - t_first) & 1) == 0); ++t) ATTN_GENERIC_STEP(t);
     for (; t + 1 < u_end; t += 2) {
-        ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1);
+        ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1, lds_b1);
         ATTN_STEP(false, 0, t);
         wait_vmem();
         __syncthreads();
-        if (t + 2 < t_end) ATTN_ISSUE_TILE_LOADS(t + 2, lds_k0, lds_v0);
+        if (t + 2 < t_end) ATTN_ISSUE_TILE_LOADS(t + 2, lds_k0, lds_v0, lds_b0);
         ATTN_STEP(false, 1, t + 1);
         wait_vmem();
         __syncthreads();
@@ -536,9 +595,27 @@ int prefill_waves(const FwdParams &p) {
     return 8;
 }
 
+// A bf16 dense bias can be loaded a tile at a time with the K/V tiles when its
+// keys are contiguous and every row starts 16-byte aligned, and one (b, h)
+// plane of it spans less than 4 GiB (the 32-bit range of a buffer load).
+bool bias_tiles_fit(const FwdParams &p) {
+    if (p.bias_sj != 1 || p.Lq < 1 || p.Lk < 1) return false;
+    if ((reinterpret_cast<uintptr_t>(p.bias) & 15u) || (p.bias_si * 2) % 16 || (p.bias_sb * 2) % 16 ||
+        (p.bias_sh * 2) % 16)
+        return false;
+    // the offsets of the last workgroup's rows (up to 255 past the last query)
+    // and keys stay below 2^32 as well
+    const int64_t plane = (((int64_t)p.Lq - 1) * p.bias_si + p.Lk) * 2;
+    const int64_t reach = ((int64_t)p.Lq + 256) * p.bias_si * 2 + ((int64_t)p.Lk + 64) * 2;
+    return p.bias_si >= p.Lk && plane > 0 && reach < ((int64_t)1 << 32);
+}
+
 template <int D, int NW>
 hipError_t launch_prefill_k(const FwdParams &p, int kind, hipStream_t stream) {
     switch (kind) {
+        case kBiasDenseBf16Tiled:
+            if constexpr (D == 128 && NW == 8) return launch_prefill_t<D, NW, kBiasDenseBf16Tiled>(p, stream);
+            return hipErrorInvalidValue;
         case kBiasNone: return launch_prefill_t<D, NW, kBiasNone>(p, stream);
         case kBiasNoneScaled: return launch_prefill_t<D, NW, kBiasNoneScaled>(p, stream);
         case kBiasAlibi: return launch_prefill_t<D, NW, kBiasAlibi>(p, stream);
@@ -558,6 +635,13 @@ hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
         case kBiasDenseF32Cap: return launch_prefill_t<D, 4, kBiasDenseF32Cap>(p, stream);
         case kBiasDenseBf16Cap: return launch_prefill_t<D, 4, kBiasDenseBf16Cap>(p, stream);
         default: break;
+    }
+    if (D == 128 && kind == kBiasDenseBf16 && bias_tiles_fit(p)) {
+        // the bias tile takes LDS beside K and V: one 8-wave workgroup per CU
+        FwdParams pt = p;
+        pt.bias_kind = kBiasDenseBf16Tiled;
+        pt.bias_plane_bytes = (uint32_t)(((int64_t)p.Lq - 1) * p.bias_si + p.Lk) * 2u;
+        return launch_prefill_k<D, 8>(pt, kBiasDenseBf16Tiled, stream);
     }
     if (D == 128 && prefill_waves(p) == 8) return launch_prefill_k<D, 8>(p, kind, stream);
     return launch_prefill_k<D, 4>(p, kind, stream);

@@ -103,6 +103,7 @@ EIGHT_WAVE_CASES = [
     (1, 64, 64, 1030, 4500, False, "alibi"),
     (1, 64, 16, 1030, 8800, True, "dense_f32"),
     (1, 64, 8, 1030, 8900, True, "none"),
+    (1, 64, 16, 1030, 8800, True, "dense_bf16"),   # bf16 bias tiles through LDS
 ]
 
 
@@ -116,8 +117,8 @@ def test_prefill_eight_wave_sampled(case):
     if bias == "alibi":
         sl = synth.alibi_slopes(Hq)
         gkw["alibi_slopes"], okw["alibi_slopes"] = sl.cuda(), sl
-    elif bias == "dense_f32":
-        bt = synth.make_dense_bias(w, (Lq, Lk), "f32")   # broadcast over batch and heads
+    elif bias in ("dense_f32", "dense_bf16"):
+        bt = synth.make_dense_bias(w, (Lq, Lk), bias[6:])   # broadcast over batch and heads
         gkw["bias"], okw["bias"] = bt.cuda(), bt.float()
     o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), causal, **gkw)
     torch.cuda.synchronize()
@@ -126,6 +127,42 @@ def test_prefill_eight_wave_sampled(case):
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, rows=rows, **okw)
     compare(o.reshape(-1, 128)[torch.from_numpy(rows).cuda()], lse.reshape(-1)[torch.from_numpy(rows).cuda()],
             O_ref, L_ref, "bf16", str(case))
+
+
+# bf16 dense bias at d = 128: rows of contiguous keys that start 16-byte
+# aligned are loaded a tile at a time into LDS beside K and V (eight-wave
+# workgroups); other layouts read each element where it is used.  Layouts:
+# contiguous [Hq, Lq, Lk]; rows padded to a longer stride (the keys past Lk in
+# a row's last chunk are padding); one [Lq, Lk] plane broadcast over batch and
+# heads; rows whose stride is not a multiple of 8 elements (the per-element path).
+DENSE_BF16_CASES = [
+    # B, Hq, Hkv, Lq, Lk, causal, layout
+    (2, 4, 2, 300, 328, True, "contiguous"),
+    (1, 3, 3, 520, 330, False, "padded"),
+    (2, 2, 1, 700, 512, True, "broadcast"),
+    (1, 2, 2, 600, 200, True, "contiguous"),    # Lq > Lk: rows that see no key
+    (1, 2, 2, 100, 333, False, "contiguous"),   # stride of 333 elements: per-element path
+    (1, 2, 2, 1, 64, False, "contiguous"),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_BF16_CASES, ids=[str(i) for i in range(len(DENSE_BF16_CASES))])
+def test_prefill_dense_bf16_layouts(case):
+    B, Hq, Hkv, Lq, Lk, causal, layout = case
+    print("dense bf16 bias case", case, flush=True)
+    w = synth.Workload("dense", B, Hq, Hkv, Lq, Lk, 128, "bf16", causal, "dense", 31 + Lq)
+    q, k, v = synth.make_qkv(w)
+    if layout == "broadcast":
+        bt = synth.make_dense_bias(w, (Lq, Lk), "bf16")
+    elif layout == "padded":
+        bt = synth.make_dense_bias(w, (Hq, Lq, Lk + 6), "bf16")[..., :Lk]
+    else:
+        bt = synth.make_dense_bias(w, (Hq, Lq, Lk), "bf16")
+    bg = bt.cuda() if layout != "padded" else synth.make_dense_bias(w, (Hq, Lq, Lk + 6), "bf16").cuda()[..., :Lk]
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), causal, bias=bg)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, bias=bt.float())
+    compare(o, lse, O_ref, L_ref, "bf16", str(case))
 
 
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(i) for i in range(len(PREFILL_CASES))])
