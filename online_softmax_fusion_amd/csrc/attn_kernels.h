@@ -9,13 +9,15 @@ namespace attn {
 
 // kBiasNoneScaled: no bias, score formed explicitly (used when the scale is not
 // positive).  The *Cap kinds add the soft cap of the scaled score.
-// kBiasDenseBf16Tiled: a bf16 dense bias whose rows are contiguous and
-// 16-byte aligned, loaded a tile at a time into LDS beside K and V (chosen by
-// the prefill launcher; never set by the host interface).
+// Two kinds are chosen by the prefill launcher and never set by the host
+// interface: kBiasDenseBf16Tiled, a bf16 dense bias whose rows are contiguous
+// and 16-byte aligned, loaded a tile at a time into LDS beside K and V; and
+// kBiasAlibiCausal, ALiBi under a causal mask with a positive scale, whose
+// bias is added to the scores by one more matrix-core product.
 enum BiasKind {
     kBiasNone = 0, kBiasAlibi = 1, kBiasDenseF32 = 2, kBiasDenseBf16 = 3, kBiasNoneScaled = 4,
     kBiasNoneCap = 5, kBiasAlibiCap = 6, kBiasDenseF32Cap = 7, kBiasDenseBf16Cap = 8,
-    kBiasDenseBf16Tiled = 9
+    kBiasDenseBf16Tiled = 9, kBiasAlibiCausal = 10
 };
 // whether a kind carries the soft cap, and its bias part
 constexpr bool bias_cap(int kind) { return kind >= kBiasNoneCap && kind <= kBiasDenseBf16Cap; }

@@ -85,10 +85,39 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                                              float &m_run, float &l_run, int kt0, int qrow, int qpos,
                                              int jmin, int jmax, float slope_l2, int b, int h, int lane) {
     using C = TileCfg<D>;
-    constexpr bool FOLD = (BIAS == kBiasNone);
+    constexpr bool AC = (BIAS == kBiasAlibiCausal);
+    constexpr bool FOLD = (BIAS == kBiasNone) || AC;
     constexpr int BK = bias_base(BIAS);
     constexpr bool CAP = bias_cap(BIAS);
     const int hh = lane >> 5;
+
+    // Causal ALiBi: every key j a row sees lies at or before the row's
+    // position, so the bias -slope |pos - j| is slope (j - P0) - slope (pos -
+    // P0) for any P0.  The second term is constant along the row and leaves
+    // the softmax unchanged (the epilogue takes it out of the LSE); the first
+    // depends on the key only, and one more matrix-core product adds it to
+    // every row's raw score: the A operand holds v_j = (slope / scale) (j -
+    // P0) split into three bf16 parts (hi + mid + lo = v_j to fp32 precision)
+    // in k = 0..2 of key row j, the B operand ones in k = 0..2.  P0 is the
+    // position of the workgroup's first row, which keeps v_j small for the
+    // keys near the rows' positions (the ones that carry the weight).
+    // slope_l2 carries slope / scale for this kind.
+    u32x4 ext_a[2], ext_b;
+    if constexpr (AC) {
+        const int wrow = ((int)threadIdx.x >> 6) * 32 + (lane & 31);   // the row's index in the workgroup
+        const int jrel = kt0 + perm32(lane & 31) - (qpos - wrow);       // key of A row r minus P0
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const float v = slope_l2 * (float)(jrel + kb * 32);
+            const uint32_t hi = pack_bf16x2(v, 0.f) & 0xffffu;
+            const float r1 = v - __uint_as_float(hi << 16);
+            const uint32_t mid = pack_bf16x2(r1, 0.f) & 0xffffu;
+            const float r2 = r1 - __uint_as_float(mid << 16);
+            const uint32_t lo = pack_bf16x2(r2, 0.f) & 0xffffu;
+            ext_a[kb] = hh == 0 ? u32x4{hi | (mid << 16), lo, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+        }
+        ext_b = hh == 0 ? u32x4{0x3f803f80u, 0x3f80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+    }
 
     // 1. S^T = K Q^T, the two 32-key blocks interleaved (two accumulation
     //    chains); the K operand reads run ahead of the matrix core (below)
@@ -111,6 +140,10 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     for (int i = 0; i < 2 * C::KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i < 2 * C::KS - RA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (AC) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(as_bf16x8(ext_a[kb]), as_bf16x8(ext_b), s[kb]);
     }
     // 2. score modifier; tile max (raw scores when the scale is folded)
     const float sc = p.scale_log2;
@@ -362,6 +395,7 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
 
     float slope_l2 = 0.f;
     if (bias_base(BIAS) == kBiasAlibi) slope_l2 = p.slopes[h] * kLog2e;
+    if (BIAS == kBiasAlibiCausal) slope_l2 = p.slopes[h] / p.scale;   // v_j per key of distance
 
     // per-lane LDS byte offsets: K operand of k-step ks at kbase ^ (ks << 5)
     // (+32 rows per key block); V transposing read of d-block db at
@@ -507,7 +541,9 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
             }
         }
         if (p.lse != nullptr && hh == 0) {
-            const float lse = (l_tot > 0.f) ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+            float lse = (l_tot > 0.f) ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+            // the row constant of the folded ALiBi bias: slope (pos - P0), P0 = q0 + Lk - Lq
+            if constexpr (BIAS == kBiasAlibiCausal) lse -= p.slopes[h] * (float)(qrow - q0);
             p.lse[((int64_t)b * p.Hq + h) * p.Lq + qrow] = lse;
         }
     }
@@ -616,6 +652,7 @@ hipError_t launch_prefill_k(const FwdParams &p, int kind, hipStream_t stream) {
         case kBiasDenseBf16Tiled:
             if constexpr (D == 128 && NW == 8) return launch_prefill_t<D, NW, kBiasDenseBf16Tiled>(p, stream);
             return hipErrorInvalidValue;
+        case kBiasAlibiCausal: return launch_prefill_t<D, NW, kBiasAlibiCausal>(p, stream);
         case kBiasNone: return launch_prefill_t<D, NW, kBiasNone>(p, stream);
         case kBiasNoneScaled: return launch_prefill_t<D, NW, kBiasNoneScaled>(p, stream);
         case kBiasAlibi: return launch_prefill_t<D, NW, kBiasAlibi>(p, stream);
@@ -635,6 +672,13 @@ hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
         case kBiasDenseF32Cap: return launch_prefill_t<D, 4, kBiasDenseF32Cap>(p, stream);
         case kBiasDenseBf16Cap: return launch_prefill_t<D, 4, kBiasDenseBf16Cap>(p, stream);
         default: break;
+    }
+    if (kind == kBiasAlibi && p.causal && p.scale > 0.f) {
+        // every visible key lies at or before its row: the bias folds into the scores
+        FwdParams pa = p;
+        pa.bias_kind = kBiasAlibiCausal;
+        if (D == 128 && prefill_waves(p) == 8) return launch_prefill_k<D, 8>(pa, kBiasAlibiCausal, stream);
+        return launch_prefill_k<D, 4>(pa, kBiasAlibiCausal, stream);
     }
     if (D == 128 && kind == kBiasDenseBf16 && bias_tiles_fit(p)) {
         // the bias tile takes LDS beside K and V: one 8-wave workgroup per CU

@@ -89,6 +89,11 @@ PREFILL_CASES = [
     (2, 16, 4, 250, 250, 128, "bf16", True, "none"),
     (1, 16, 16, 200, 230, 128, "bf16", True, "alibi"),
     (1, 16, 4, 1030, 5150, 128, "bf16", True, "none"),
+    # causal ALiBi (the bias folded into the scores by one more matrix product):
+    # d = 64, end-aligned Lq < Lk, Lq > Lk (rows that see no key), GQA
+    (2, 4, 4, 260, 260, 64, "bf16", True, "alibi"),
+    (1, 4, 2, 150, 700, 128, "bf16", True, "alibi"),
+    (1, 2, 2, 300, 140, 128, "bf16", True, "alibi"),
 ]
 
 
@@ -192,6 +197,7 @@ MOD_CASES = [
     (1, 2, 2, 160, 160, 128, "bf16", True, "none", 30.0, (50, -1)),    # loose cap + window
     (1, 2, 2, 150, 333, 128, "f32", True, "none", 4.0, (60, -1)),      # fp32 path
     (1, 2, 2, 97, 200, 64, "f32", False, "alibi", 1.5, (10, 10)),
+    (1, 4, 4, 300, 420, 128, "bf16", True, "alibi", 0.0, (90, -1)),    # causal ALiBi + window (folded form)
 ]
 
 
