@@ -756,10 +756,10 @@ def traffic_table(d):
         # kernel, name match, workload, sources, algorithmic bytes, grid work-items, counter runs
         # (the C2 entry names its 4-wave form: the backward leg's non-causal forward runs the
         # 8-wave form on the same grid; the template's third argument is the score modifier:
-        # 0 none, 1 ALiBi, 9 dense bf16 bias loaded in tiles)
+        # 0 none, 10 causal ALiBi folded into the scores, 9 dense bf16 bias loaded in tiles)
         ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 4, 0, true>",), wp, PREFILL_SOURCES, pf(wp), pgrid(wp),
          ""),
-        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 1, true>"), w3, PREFILL_SOURCES, pf(w3), pgrid(w3),
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 10, true>"), w3, PREFILL_SOURCES, pf(w3), pgrid(w3),
          ""),
         ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 8, 9, true>",), w3d, PREFILL_SOURCES,
          pf(w3d) + dense_bias_bytes(w3d), pgrid(w3d), ""),
