@@ -173,7 +173,12 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
             float x = s[kb][e];
             if (!FOLD) {
                 x *= sc;
-                if (CAP) x = soft_cap(x, p.cap_l2, p.cap_k, p.cap_inv);   // in log2 units
+                if (CAP) {   // in log2 units
+                    if constexpr (BIAS == kBiasNoneCapExp)
+                        x = soft_cap_exp(x, p.cap_l2, p.cap_k);
+                    else
+                        x = soft_cap(x, p.cap_l2, p.cap_k, p.cap_inv);
+                }
                 if (BK == kBiasAlibi) {
                     x = fmaf(-slope_l2, fabsf(dbase - (float)(kb * 32 + (e >> 3) * 16 + (e & 7))), x);
                 } else if (BK == kBiasDenseBf16Tiled) {
@@ -667,7 +672,9 @@ hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
     // the folded-scale path needs a positive scale; otherwise form the score explicitly
     const int kind = (p.bias_kind == kBiasNone && !(p.scale_log2 > 0.f)) ? kBiasNoneScaled : p.bias_kind;
     switch (kind) {   // the soft-capped kinds run with four waves only
-        case kBiasNoneCap: return launch_prefill_t<D, 4, kBiasNoneCap>(p, stream);
+        case kBiasNoneCap:
+            if (p.softcap <= 64.f) return launch_prefill_t<D, 4, kBiasNoneCapExp>(p, stream);
+            return launch_prefill_t<D, 4, kBiasNoneCap>(p, stream);
         case kBiasAlibiCap: return launch_prefill_t<D, 4, kBiasAlibiCap>(p, stream);
         case kBiasDenseF32Cap: return launch_prefill_t<D, 4, kBiasDenseF32Cap>(p, stream);
         case kBiasDenseBf16Cap: return launch_prefill_t<D, 4, kBiasDenseBf16Cap>(p, stream);

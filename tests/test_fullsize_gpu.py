@@ -46,7 +46,8 @@ def check_heads(w, q, k, v, o, lse, heads, rows, slopes=None, bias=None):
             kw["alibi_slopes"] = slopes[h:h + 1]
         if bias is not None:
             kw["bias"] = bias[h:h + 1].float().cpu()
-        O_ref, L_ref = oracle.attention(qh, kh, vh, w.softmax_scale(), w.causal, rows=rows, **kw)
+        O_ref, L_ref = oracle.attention(qh, kh, vh, w.softmax_scale(), w.causal, rows=rows, softcap=w.softcap,
+                                        window=w.window, **kw)
         sel = slice(None) if rows is None else rows
         og = o[b, h, sel].float().cpu().numpy()
         lg = lse[b, h, sel].cpu().numpy()
@@ -59,14 +60,15 @@ def check_heads(w, q, k, v, o, lse, heads, rows, slopes=None, bias=None):
     print("%s: worst O err %.3e, worst LSE err %.3e" % (w.name, worst_o, worst_l), flush=True)
 
 
-@pytest.mark.parametrize("w", [synth.C2_CAUSAL, synth.C3_ALIBI, synth.C5_PREFILL], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [synth.C2_CAUSAL, synth.C3_ALIBI, synth.C5_PREFILL, synth.SOFTCAP_PREFILL,
+                               synth.WINDOW_PREFILL], ids=lambda w: w.name)
 def test_prefill_fullsize_sampled(w):
     print("full-size prefill", w.name, flush=True)
     rng = np.random.default_rng(w.seed)
     q, k, v = synth.make_qkv(w, device="cuda")
     slopes = synth.alibi_slopes(w.Hq) if w.bias == "alibi" else None
     kw = {"alibi_slopes": slopes.cuda()} if slopes is not None else {}
-    o, lse = attn.attn_fwd_prefill(q, k, v, w.softmax_scale(), w.causal, **kw)
+    o, lse = attn.attn_fwd_prefill(q, k, v, w.softmax_scale(), w.causal, softcap=w.softcap, window=w.window, **kw)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2)} |

@@ -198,6 +198,8 @@ MOD_CASES = [
     (1, 2, 2, 150, 333, 128, "f32", True, "none", 4.0, (60, -1)),      # fp32 path
     (1, 2, 2, 97, 200, 64, "f32", False, "alibi", 1.5, (10, 10)),
     (1, 4, 4, 300, 420, 128, "bf16", True, "alibi", 0.0, (90, -1)),    # causal ALiBi + window (folded form)
+    (1, 4, 4, 300, 300, 128, "bf16", True, "none", 64.0, None),        # largest cap of the exp-only form
+    (1, 4, 4, 300, 300, 128, "bf16", True, "none", 64.5, None),        # smallest cap of the exact form
 ]
 
 
