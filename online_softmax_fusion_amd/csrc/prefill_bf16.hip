@@ -86,7 +86,12 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                                              int jmin, int jmax, float slope_l2, int b, int h, int lane) {
     using C = TileCfg<D>;
     constexpr bool AC = (BIAS == kBiasAlibiCausal);
-    constexpr bool FOLD = (BIAS == kBiasNone) || AC;
+    // CE: the soft cap by the exp form with a positive scale: the capped score
+    // is increasing in the raw one, so the tile max is taken on raw scores and
+    // capped once, and P = 2^(c - m - 2c / (2^(s * scale * k2) + 1)) is formed
+    // from the raw score directly
+    constexpr bool CE = (BIAS == kBiasNoneCapExp);
+    constexpr bool FOLD = (BIAS == kBiasNone) || AC || CE;
     constexpr int BK = bias_base(BIAS);
     constexpr bool CAP = bias_cap(BIAS);
     const int hh = lane >> 5;
@@ -205,6 +210,9 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     }
     mx = xor32_max(mx);
     if (FOLD) mx *= sc;   // sc > 0: max commutes with the scaling
+    if constexpr (CE) {
+        if (mx != -INFINITY) mx = soft_cap_exp(mx, p.cap_l2, p.cap_k);
+    }
 
     // 3. lazy repair of l and O when the max has grown by more than TAU
     if (__any(mx > m_run + kTau)) {
@@ -228,7 +236,17 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             float p0, p1;
-            if (FOLD) {
+            if constexpr (CE) {
+                // capped - m = (c - m) - 2c / (2^(s * sc * k2) + 1); a masked score
+                // (-inf) would give 2^(-c - m), so it is zeroed explicitly
+                const float cm = p.cap_l2 - m_use, c2 = -2.f * p.cap_l2, u = sc * p.cap_k;
+                p0 = exp2_fast(fmaf(c2, __builtin_amdgcn_rcpf(exp2_fast(s[kb][e] * u) + 1.f), cm));
+                p1 = exp2_fast(fmaf(c2, __builtin_amdgcn_rcpf(exp2_fast(s[kb][e + 1] * u) + 1.f), cm));
+                if (MASK) {
+                    if (s[kb][e] == -INFINITY) p0 = 0.f;
+                    if (s[kb][e + 1] == -INFINITY) p1 = 0.f;
+                }
+            } else if (FOLD) {
                 p0 = exp2_fast(fmaf(s[kb][e], sc, -m_use));
                 p1 = exp2_fast(fmaf(s[kb][e + 1], sc, -m_use));
             } else {
@@ -673,7 +691,7 @@ hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
     const int kind = (p.bias_kind == kBiasNone && !(p.scale_log2 > 0.f)) ? kBiasNoneScaled : p.bias_kind;
     switch (kind) {   // the soft-capped kinds run with four waves only
         case kBiasNoneCap:
-            if (p.softcap <= 64.f) return launch_prefill_t<D, 4, kBiasNoneCapExp>(p, stream);
+            if (p.softcap <= 64.f && p.scale > 0.f) return launch_prefill_t<D, 4, kBiasNoneCapExp>(p, stream);
             return launch_prefill_t<D, 4, kBiasNoneCap>(p, stream);
         case kBiasAlibiCap: return launch_prefill_t<D, 4, kBiasAlibiCap>(p, stream);
         case kBiasDenseF32Cap: return launch_prefill_t<D, 4, kBiasDenseF32Cap>(p, stream);
