@@ -514,6 +514,72 @@ __device__ __forceinline__ void dkdv_rows(const FwdParams &p, const char *lq, co
     }
 }
 
+// The same for a wave whose keys' K and V rows sit in LDS (rows read like the
+// Q rows: key row kr of lane r at kvb ^ (ks << 5)) instead of registers.
+template <int D, int BIAS>
+__device__ __forceinline__ void dkdv_rows_kv(const FwdParams &p, const char *lq, const char *ldo, const float *llse,
+                                             const float *ldel, int rbase, int tbase, const char *lk, const char *lv,
+                                             int kvb, f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32], int qs0,
+                                             int i0, int key, int imin, int imax, bool masked, float slope_l2, int b,
+                                             int h, int lane) {
+    using C = BwdCfg<D>;
+    const int hh = lane >> 5;
+    // S = Q K^T, dP = dO V^T (query perm32(r) in matrix-core row r)
+    f32x16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        s = mfma32(as_bf16x8(load16(lq + ((rbase ^ (ks << 5)) + qs0 * C::RB))), as_bf16x8(load16(lk + (kvb ^ (ks << 5)))),
+                   s);
+        dp = mfma32(as_bf16x8(load16(ldo + ((rbase ^ (ks << 5)) + qs0 * C::RB))),
+                    as_bf16x8(load16(lv + (kvb ^ (ks << 5)))), dp);
+    }
+    // schedule: the two operand reads of each product two products ahead of it
+    {
+        constexpr int KA = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KA, 2);
+#pragma unroll
+        for (int i = 0; i < 2 * C::KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            if (i < 2 * C::KS - KA) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        }
+    }
+    f32x4 L[4], Dl[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int rr = qs0 + (g >> 1) * 16 + hh * 8 + (g & 1) * 4;
+        L[g] = *reinterpret_cast<const f32x4 *>(llse + rr);
+        Dl[g] = *reinterpret_cast<const f32x4 *>(ldel + rr);
+    }
+    const int ibase = i0 + qs0 + hh * 8;
+    uint32_t pk[8], dk[8];
+    if (masked)
+        dkdv_scores<BIAS, true>(p, s, dp, L, Dl, ibase, key, imin, imax, slope_l2, b, h, pk, dk);
+    else
+        dkdv_scores<BIAS, false>(p, s, dp, L, Dl, ibase, key, imin, imax, slope_l2, b, h, pk, dk);
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 bp_ = as_bf16x8(u32x4{pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]});
+        const bf16x8 bd_ = as_bf16x8(u32x4{dk[4 * kk], dk[4 * kk + 1], dk[4 * kk + 2], dk[4 * kk + 3]});
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            dvacc[db] = mfma32(tr_operand<D>(ldo, tbase, db, qs0 + kk * 16), bp_, dvacc[db]);
+            dkacc[db] = mfma32(tr_operand<D>(lq, tbase, db, qs0 + kk * 16), bd_, dkacc[db]);
+        }
+    }
+    {
+        constexpr int KV = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KV, 3);
+#pragma unroll
+        for (int i = 0; i < 4 * C::DB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+            if (i < 4 * C::DB - KV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+        }
+    }
+}
+
 template <int D, int NW, int BIAS>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
     using C = BwdCfg<D>;
@@ -661,6 +727,180 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
     }
 }
 
+// dK/dV with two waves per SIMD (d = 128): eight waves per workgroup in four
+// pairs, each pair owning 32 of the workgroup's 128 keys.  The keys' K and V
+// rows sit in LDS (64 KiB, loaded once) instead of registers, which brings a
+// wave under the 256 registers that two waves per SIMD allow; the two waves of
+// a pair take alternate 32-row halves of every streamed Q/dO tile and add
+// their partial dK, dV through LDS at the end, so the sums keep one order
+// (bitwise deterministic).
+template <int D, int BIAS>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdParams bp) {
+    using C = BwdCfg<D>;
+    const FwdParams &p = bp.f;
+    constexpr int NW = 8;
+    constexpr int BK = 128;              // keys per workgroup
+    constexpr int BQ = C::BT;            // query rows per streamed tile
+    constexpr int T = NW * 64;
+    constexpr int STAGE = 2 * C::TILE + 2 * BQ * 4;
+    static_assert(BK == 2 * C::BT, "the key block is two tiles");
+    static_assert(D * 64 * 4 <= 2 * C::TILE, "a pair's partial sums fit in half of the K/V area");
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char kvs[4 * C::TILE];   // K rows 0..127, then V rows 0..127
+
+    const int nkt = (p.Lk + BK - 1) / BK;
+    const WorkItem wi = xcd_work_item(nkt, p.causal && !p.window, p.num_xcds);
+    const int bhk = wi.head;
+    const int kt = wi.rank;
+    const int b = bhk / p.Hkv;
+    const int hk = bhk - b * p.Hkv;
+    const int k0 = kt * BK;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave >> 1;
+    const int half = wave & 1;
+    const int lane = tid & 63;
+    const int r = lane & 31;
+    const int hh = lane >> 5;
+    const int key = k0 + pair * 32 + r;
+    int imin, imax;
+    query_range(p, key, imin, imax);
+    const int kw0 = k0 + pair * 32;
+    const int kwl = min(kw0 + 31, p.Lk - 1);
+    int wimin = 0, wimax = -1, unused;
+    if (kw0 < p.Lk) {
+        query_range(p, kw0, wimin, unused);
+        query_range(p, kwl, unused, wimax);
+    }
+    const int klast = min(k0 + BK, p.Lk) - 1;
+    int gimin0, gimax0, gimin1, gimax1;
+    query_range(p, k0, gimin0, gimax0);
+    query_range(p, klast, gimin1, gimax1);
+    int t_first = 0, t_end = 0;
+    if (gimax1 >= gimin0 && gimax1 >= 0) {
+        t_first = gimin0 / BQ;
+        t_end = gimax1 / BQ + 1;
+    }
+    int u_first = max(t_first, (gimin1 + BQ - 1) / BQ);
+    int u_end = min(t_end, gimax0 >= 0 ? (gimax0 + 1) / BQ : 0);
+    if (k0 + BK > p.Lk || gimax1 < gimin1 || gimax0 < gimin0) u_end = u_first;   // a partial key tile: all masked
+    const int nt = t_end - t_first;
+    const int iters = nt * p.G;
+
+    const uint16_t *kp = static_cast<const uint16_t *>(p.k) + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
+    const uint16_t *vp = static_cast<const uint16_t *>(p.v) + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+    const int rbase = C::row_base(lane);
+    const int tbase = C::tr_base(lane);
+    const int kvb = C::off(pair * 32 + r, hh);
+    const uint32_t ql_bytes = (uint32_t)p.q_sl * 2u;
+    const uint32_t dl_bytes = (uint32_t)bp.do_sl * 2u;
+    const uint32_t qgoff = tile_goff<D>(wave, lane, ql_bytes);
+    const uint32_t dgoff = tile_goff<D>(wave, lane, dl_bytes);
+    const uint32_t lds0 = lds_addr(smem);
+
+    // the workgroup's K and V rows (rows past Lk read as zero; no row sees those keys)
+    {
+        const uint32_t kl_bytes = (uint32_t)p.k_sl * 2u;
+        const uint32_t vl_bytes = (uint32_t)p.v_sl * 2u;
+        const uint32_t kvs0 = lds_addr(kvs);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int kr0 = k0 + t * C::BT;
+            const int nv = min(C::BT, p.Lk - kr0);
+            if (nv > 0) {
+                dma_tile<D, T>(kp + (int64_t)kr0 * p.k_sl, kl_bytes, nv, kvs0 + t * C::TILE, wave,
+                               tile_goff<D>(wave, lane, kl_bytes));
+                dma_tile<D, T>(vp + (int64_t)kr0 * p.v_sl, vl_bytes, nv, kvs0 + (2 + t) * C::TILE, wave,
+                               tile_goff<D>(wave, lane, vl_bytes));
+            }
+        }
+    }
+
+    f32x16 dkacc[C::DB], dvacc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dkacc[db][e] = dvacc[db][e] = 0.f;
+
+    auto issue = [&](int it, int st) {
+        const int hi = it / nt;
+        const int hq = hk * p.G + hi;
+        const int q0 = (t_first + it - hi * nt) * BQ;
+        const int nv = min(BQ, p.Lq - q0);
+        const uint32_t dst = lds0 + st * STAGE;
+        dma_tile<D, T>(static_cast<const uint16_t *>(p.q) + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh +
+                           (int64_t)q0 * p.q_sl, ql_bytes, nv, dst, wave, qgoff);
+        dma_tile<D, T>(static_cast<const uint16_t *>(bp.dout) + (int64_t)b * bp.do_sb + (int64_t)hq * bp.do_sh +
+                           (int64_t)q0 * bp.do_sl, dl_bytes, nv, dst + C::TILE, wave, dgoff);
+        const int64_t rw = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
+        if (wave == 0) dma4(rsrc_words(bp.lse_l2 + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE, lane * 4);
+        if (wave == 1) dma4(rsrc_words(bp.delta + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE + BQ * 4, lane * 4);
+    };
+    auto step = [&](bool masked, int it, int st) {
+        const int hi = it / nt;
+        const int hq = hk * p.G + hi;
+        const int q0 = (t_first + it - hi * nt) * BQ;
+        if (masked && !(wimax >= wimin && q0 <= wimax && q0 + BQ - 1 >= wimin)) return;
+        const float sl = bias_base(BIAS) == kBiasAlibi ? p.slopes[hq] * kLog2e : 0.f;
+        const char *sb = smem + st * STAGE;
+        const float *ll = reinterpret_cast<const float *>(sb + 2 * C::TILE);
+        dkdv_rows_kv<D, BIAS>(p, sb, sb + C::TILE, ll, ll + BQ, rbase, tbase, kvs, kvs + 2 * C::TILE, kvb, dkacc,
+                              dvacc, half * 32, q0, key, imin, imax, masked, sl, b, hq, lane);
+    };
+
+    if (iters > 0) issue(0, 0);
+    wait_all_loads();
+    __syncthreads();
+    for (int it = 0; it < iters; ++it) {
+        const int st = it & 1;
+        if (it + 1 < iters) issue(it + 1, st ^ 1);
+        const int tq = t_first + it % nt;
+        step(tq < u_first || tq >= u_end, it, st);
+        wait_all_loads();
+        __syncthreads();
+    }
+
+    // the pair's two partial sums: the second wave leaves its accumulators in
+    // LDS (lane-interleaved), the first adds them in
+    float *red = pair < 2 ? reinterpret_cast<float *>(kvs) + pair * (D * 64)
+                          : reinterpret_cast<float *>(smem) + (pair - 2) * (D * 64);
+    if (half == 1) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                red[((db * 16 + e) * 2) * 64 + lane] = dkacc[db][e];
+                red[((db * 16 + e) * 2 + 1) * 64 + lane] = dvacc[db][e];
+            }
+    }
+    __syncthreads();
+    if (half == 1 || key >= p.Lk) return;
+    const int64_t kb = (int64_t)b * bp.dk_sb + (int64_t)hk * bp.dk_sh + (int64_t)key * bp.dk_sl;
+    const int64_t vb = (int64_t)b * bp.dv_sb + (int64_t)hk * bp.dv_sh + (int64_t)key * bp.dv_sl;
+    const float sc = p.scale;
+    // one d block at a time (a compiler barrier between blocks keeps the
+    // partner's values from being read all at once beside the accumulators)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            dkacc[db][e] += red[((db * 16 + e) * 2) * 64 + lane];
+            dvacc[db][e] += red[((db * 16 + e) * 2 + 1) * 64 + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = db * 32 + i * 8 + hh * 4;
+            store4(bp.dk, kb + d0, bp.grad_bf16, dkacc[db][4 * i] * sc, dkacc[db][4 * i + 1] * sc,
+                   dkacc[db][4 * i + 2] * sc, dkacc[db][4 * i + 3] * sc);
+            store4(bp.dv, vb + d0, bp.grad_bf16, dvacc[db][4 * i], dvacc[db][4 * i + 1], dvacc[db][4 * i + 2],
+                   dvacc[db][4 * i + 3]);
+        }
+        asm volatile("" ::: "memory");
+    }
+}
+
 template <int D, int BIAS>
 hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
     constexpr int NW = 4;
@@ -675,7 +915,13 @@ hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     if (kv_blocks > 0) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, BIAS>), dim3((unsigned)kv_blocks), dim3(NW * 64), 0, stream, p);
+        // d = 128: the paired-wave form (128 keys per workgroup as well); with
+        // ALiBi its distance terms do not fit the 256 registers, and it keeps
+        // one wave per SIMD
+        if constexpr (D == 128 && bias_base(BIAS) != kBiasAlibi)
+            hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, BIAS>), dim3((unsigned)kv_blocks), dim3(512), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, BIAS>), dim3((unsigned)kv_blocks), dim3(NW * 64), 0, stream, p);
         return hipGetLastError();
     }
     return hipSuccess;
