@@ -85,7 +85,7 @@ def test_dkdv_loop_keeps_accumulators_in_place(tmp_path):
     dK/dV kernel only where it zeroes its accumulators (one v_accvgpr_write of
     0, copied to the others), never next to matrix-core work."""
     asm = device_asm("bwd_bf16.hip", tmp_path)
-    kernels = list(re.finditer(r"^(_ZN4attn\w*bwd_dkdv_kernel\w*):", asm, flags=re.M))
+    kernels = list(re.finditer(r"^(_ZN4attn\w*bwd_dkdv_(?:pair_)?kernel\w*):", asm, flags=re.M))
     assert kernels
     for m in kernels:
         body = asm[m.end():asm.index("s_endpgm", m.end())]
