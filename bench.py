@@ -772,9 +772,9 @@ def traffic_table(d):
         # dQ: reads Q, dO, O, LSE, K, V; writes dQ, Delta, LSE*log2(e)
         ("bwd_dq_kernel", ("bwd_dq_kernel",), wbk, BWD_SOURCES, 4 * q_e + rows4 + 2 * kv_e + 2 * rows4,
          (wbk.Lq // 128) * wbk.B * wbk.Hq * 256, ""),
-        # dK/dV: reads Q, dO, Delta, LSE*log2(e), K, V; writes dK, dV
-        ("bwd_dkdv_kernel", ("bwd_dkdv_kernel",), wbk, BWD_SOURCES, 2 * q_e + 2 * rows4 + 4 * kv_e,
-         (wbk.Lk // 128) * wbk.B * wbk.Hkv * 256, ""),
+        # dK/dV (the paired-wave kernel at d = 128): reads Q, dO, Delta, LSE*log2(e), K, V; writes dK, dV
+        ("bwd_dkdv_pair_kernel", ("bwd_dkdv_pair_kernel",), wbk, BWD_SOURCES, 2 * q_e + 2 * rows4 + 4 * kv_e,
+         (wbk.Lk // 128) * wbk.B * wbk.Hkv * 512, ""),
         ("l2norm_onepass_kernel", ("l2norm_onepass_kernel",), wl, L2NORM_SOURCES, l2norm_bytes(wl.rows, wl.H, 2, 2),
          (wl.rows // 4) * 256, ""),
         # split path: the partial kernel reads x and writes one partial per chunk; the scale kernel
@@ -963,11 +963,11 @@ def main():
         result["backward"] = {
             "workload": wb.name, "causal": wb.causal, "value": round(b_flops / b_step_s / 1e12, 2),
             "unit": "TFLOP/s", "ms_per_step": round(b_step_s * 1e3, 4),
-            "roofline": {"kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "bound": "mfma",
+            "roofline": {"kernel": "bwd_dq_kernel + bwd_dkdv_pair_kernel", "bound": "mfma",
                          "achieved": round(b_kern_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(b_kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": _sum_traffic([("bwd_dq_kernel", wb.name, BWD_SOURCES),
-                                                  ("bwd_dkdv_kernel", wb.name, BWD_SOURCES)])}}
+                                                  ("bwd_dkdv_pair_kernel", wb.name, BWD_SOURCES)])}}
     if not args.no_cpu_baseline and "prefill" in legs:
         result["cpu_baseline"] = cpu_baseline(wp, args.cpu_budget)
     else:
