@@ -538,7 +538,10 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
                     *reinterpret_cast<f32x4 *>(op + db * 32 + i * 8 + hh * 4) =
                         f32x4{oacc[db][4 * i], oacc[db][4 * i + 1], oacc[db][4 * i + 2], oacc[db][4 * i + 3]};
             if (hh == 0) {
-                p.m_part[prow] = (m_run == -INFINITY) ? -INFINITY : m_run * kLn2;
+                float mp = (m_run == -INFINITY) ? -INFINITY : m_run * kLn2;
+                // the folded ALiBi's row constant, as in the LSE of the plain prefill
+                if constexpr (BIAS == kBiasAlibiCausal) mp -= p.slopes[h] * (float)(qrow - q0);
+                p.m_part[prow] = mp;
                 p.l_part[prow] = l_tot;
             }
         }
@@ -600,10 +603,18 @@ hipError_t launch_prefill_part_d(const FwdParams &p, hipStream_t stream) {
     switch (kind) {
         case kBiasNone: return launch_prefill_part_t<D, kBiasNone>(p, stream);
         case kBiasNoneScaled: return launch_prefill_part_t<D, kBiasNoneScaled>(p, stream);
-        case kBiasAlibi: return launch_prefill_part_t<D, kBiasAlibi>(p, stream);
+        case kBiasAlibi:
+            if (p.causal && p.scale > 0.f) {   // the folded form, as in the plain prefill
+                FwdParams pa = p;
+                pa.bias_kind = kBiasAlibiCausal;
+                return launch_prefill_part_t<D, kBiasAlibiCausal>(pa, stream);
+            }
+            return launch_prefill_part_t<D, kBiasAlibi>(p, stream);
         case kBiasDenseF32: return launch_prefill_part_t<D, kBiasDenseF32>(p, stream);
         case kBiasDenseBf16: return launch_prefill_part_t<D, kBiasDenseBf16>(p, stream);
-        case kBiasNoneCap: return launch_prefill_part_t<D, kBiasNoneCap>(p, stream);
+        case kBiasNoneCap:
+            if (p.softcap <= 64.f && p.scale > 0.f) return launch_prefill_part_t<D, kBiasNoneCapExp>(p, stream);
+            return launch_prefill_part_t<D, kBiasNoneCap>(p, stream);
         case kBiasAlibiCap: return launch_prefill_part_t<D, kBiasAlibiCap>(p, stream);
         case kBiasDenseF32Cap: return launch_prefill_part_t<D, kBiasDenseF32Cap>(p, stream);
         case kBiasDenseBf16Cap: return launch_prefill_part_t<D, kBiasDenseBf16Cap>(p, stream);

@@ -305,6 +305,31 @@ def test_prefill_constant_v():
     assert float((o.float() - 0.75).abs().max()) <= 1.5e-2
 
 
+@pytest.mark.parametrize("causal,Lq,Lk", [(True, 300, 300), (True, 200, 460), (False, 260, 300)])
+def test_alibi_matches_dense_bias_of_its_values(causal, Lq, Lk):
+    """ALiBi from the slopes (under a causal mask the folded form, whose bias
+    enters through one more matrix product) against the same values given as a
+    dense fp32 bias: the two paths agree within the bf16 bars; and slopes of 0
+    give the unbiased result."""
+    w, q, k, v, _, _ = inputs(1, 4, 4, Lq, Lk, 128, "bf16", causal, "alibi", seed=8 + Lq)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    sl = synth.alibi_slopes(4)
+    dense = synth.alibi_bias_tensor(w.with_(bias="dense"), "f32").cuda()
+    o_a, l_a = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), causal, alibi_slopes=sl.cuda(),
+                                     out_dtype=torch.float32)
+    o_d, l_d = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), causal, bias=dense, out_dtype=torch.float32)
+    o_0, l_0 = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), causal, alibi_slopes=torch.zeros(4).cuda(),
+                                     out_dtype=torch.float32)
+    o_n, l_n = attn.attn_fwd_prefill(qg, kg, vg, w.softmax_scale(), causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    fin = torch.isfinite(l_a)
+    assert torch.equal(fin, torch.isfinite(l_d))
+    assert float((o_a - o_d).abs().max()) <= 1.5e-2
+    assert float((l_a[fin] - l_d[fin]).abs().max()) <= 1e-3
+    assert float((o_0 - o_n).abs().max()) <= 1.5e-2
+    assert float((l_0[fin] - l_n[fin]).abs().max()) <= 1e-3
+
+
 def test_prefill_deterministic():
     w, q, k, v, _, _ = inputs(1, 4, 4, 300, 300, 128, "bf16", True, "alibi", seed=4)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()

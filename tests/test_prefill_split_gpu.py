@@ -36,6 +36,8 @@ CASES = [
     (1, 1, 1, 64, 100, 128, False, "none", 0.0, None, 8),      # chunks 2..7 empty
     (1, 2, 2, 300, 150, 128, True, "none", 0.0, None, 2),      # Lq > Lk: rows without keys
     (1, 4, 4, 1, 4100, 128, False, "none", 0.0, None, 16),     # one query row
+    (1, 4, 2, 200, 1500, 128, True, "alibi", 0.0, None, 3),    # causal ALiBi, folded form
+    (1, 2, 2, 140, 900, 128, True, "none", 50.0, None, 3),     # cap by the exp form
 ]
 
 
