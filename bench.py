@@ -416,6 +416,22 @@ def time_decode(w, steps, warmup, warm_s=1.0):
     durs = sorted(a.elapsed_time(b) for a, b in ev)
     avg_ms = sum(durs) / len(durs)
 
+    # the same step as one attn_fwd call (the planner picks the same split-K
+    # plan here; one binding call instead of two), with its workspace reused
+    fwd_step_s = None
+    plan = attn.attn_fwd_choose_plan(q, k, v, scale, w.causal)
+    if plan.method == attn.ATTN_PLAN_SPLITK and plan.num_splits == S:
+        wsb = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device="cuda")
+        fstep = lambda i: attn.attn_fwd(q, kvs[i % copies][0], kvs[i % copies][1], scale, w.causal, out=o, lse=lse,
+                                        workspace=wsb)
+        warm_up(fstep, warmup, 0.2)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fstep(i)
+        torch.cuda.synchronize()
+        fwd_step_s = (time.perf_counter() - t0) / steps
+        del wsb
+
     # the same steps replayed from a HIP graph (one graph holds one step per
     # K/V copy), which removes the host launch cost between the two kernels
     graph_step_s = None
@@ -446,13 +462,15 @@ def time_decode(w, steps, warmup, warm_s=1.0):
     except RuntimeError as e:   # graph capture is an extra measurement; the eager step stands without it
         log("decode: graph replay not measured (%s)" % e)
 
-    log("decode: %s S=%d, step %.4f ms (graph replay %s ms), partial kernel avg %.4f ms (p10 %.4f, p90 %.4f)" %
-        (w.name, S, wall * 1e3, "%.4f" % (graph_step_s * 1e3) if graph_step_s else "-", avg_ms,
+    log("decode: %s S=%d, step %.4f ms (attn_fwd %s ms, graph replay %s ms), partial kernel avg %.4f ms "
+        "(p10 %.4f, p90 %.4f)" %
+        (w.name, S, wall * 1e3, "%.4f" % (fwd_step_s * 1e3) if fwd_step_s else "-",
+         "%.4f" % (graph_step_s * 1e3) if graph_step_s else "-", avg_ms,
          durs[len(durs) // 10], durs[(9 * len(durs)) // 10]))
     del q, k, v, kvs, op, mp, lp, o, lse
     torch.cuda.empty_cache()
     return {"step_s": wall, "kern_s": avg_ms * 1e-3, "S": S, "durs": durs, "sclk": sclk, "copies": copies,
-            "graph_step_s": graph_step_s}
+            "graph_step_s": graph_step_s, "fwd_step_s": fwd_step_s}
 
 
 def time_backward(w, steps, warmup, warm_s=1.0):
@@ -845,6 +863,9 @@ def decode_leg_json(w, r):
             "unit": "GB/s", "ms_per_step": round(r["step_s"] * 1e3, 4),
             "graph_replay": None if not gs else {"ms_per_step": round(gs * 1e3, 4),
                                                  "value": round(d_bytes / gs / 1e9, 1), "unit": "GB/s"},
+            "attn_fwd_step": None if not r.get("fwd_step_s") else {
+                "ms_per_step": round(r["fwd_step_s"] * 1e3, 4), "value": round(d_bytes / r["fwd_step_s"] / 1e9, 1),
+                "unit": "GB/s"},
             "kernel_ms": _stats_ms(r["durs"]),
             "sclk": r["sclk"],
             "roofline": {"kernel": "decode_bf16_kernel", "bound": "hbm", "achieved": round(kgbs, 1),
