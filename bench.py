@@ -832,7 +832,8 @@ def prefill_leg_json(w, r):
     bias bytes make it bound by HBM, and both fractions are given)."""
     flops = r["flops"]
     kern_tf = flops / r["kern_s"] / 1e12
-    leg = {"workload": w.name, "bias": w.bias, "value": round(flops / r["step_s"] / 1e12, 2), "unit": "TFLOP/s",
+    leg = {"workload": w.name, "bias": w.bias, "seed": w.seed, "value": round(flops / r["step_s"] / 1e12, 2),
+           "unit": "TFLOP/s",
            "ms_per_step": round(r["step_s"] * 1e3, 4), "kernel_ms": _stats_ms(r["durs"]), "sclk": r["sclk"]}
     traffic = measured_traffic("prefill_bf16_kernel", w.name, PREFILL_SOURCES)
     if w.bias == "dense":
@@ -859,7 +860,7 @@ def decode_leg_json(w, r):
     gbs = d_bytes / r["step_s"] / 1e9
     kgbs = k_bytes / r["kern_s"] / 1e9
     gs = r.get("graph_step_s")
-    return {"workload": w.name, "splits": S, "kv_copies_rotated": r["copies"], "value": round(gbs, 1),
+    return {"workload": w.name, "seed": w.seed, "splits": S, "kv_copies_rotated": r["copies"], "value": round(gbs, 1),
             "unit": "GB/s", "ms_per_step": round(r["step_s"] * 1e3, 4),
             "graph_replay": None if not gs else {"ms_per_step": round(gs * 1e3, 4),
                                                  "value": round(d_bytes / gs / 1e9, 1), "unit": "GB/s"},
@@ -946,7 +947,7 @@ def main():
         "metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 inputs)",
-        "config": {"workload": wp.name, "B": wp.B, "H": wp.Hq, "Lq": wp.Lq, "Lk": wp.Lk, "D": wp.D,
+        "config": {"workload": wp.name, "seed": wp.seed, "B": wp.B, "H": wp.Hq, "Lq": wp.Lq, "Lk": wp.Lk, "D": wp.D,
                    "causal": wp.causal, "bias": wp.bias, "softcap": wp.softcap,
                    "window": list(wp.window) if wp.window else None, "parallelism": "single GPU"},
     }
