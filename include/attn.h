@@ -29,7 +29,12 @@
  *   Causal       aligned to the end of the keys: key j is visible to query row
  *                i iff j <= i + (Lk - Lq).  For Lq == Lk this is the lower
  *                triangle; a single decode query (Lq = 1) sees every key.
- *   ALiBi        bias_ij = -alibi_slopes[h] * |i + (Lk - Lq) - j|.
+ *   ALiBi        bias_ij = -alibi_slopes[h] * |i + (Lk - Lq) - j|.  With the
+ *                causal mask and bf16 inputs the bias enters the key-query
+ *                product as one more matrix-core step, relative to the position
+ *                of each group of 32 rows; its rounding grows with the slope:
+ *                for |slope| <= 64 it stays below 1e-3 on LSE and 1.5e-2 on O
+ *                against an exact evaluation (ALiBi's own slopes are at most 1).
  *   Output       O_i = sum_j softmax(s_i)_j v_j;  LSE_i = ln sum_j exp(s_ij)
  *                (natural log).  A row with no visible key gets O_i = 0 and
  *                LSE_i = -inf (never NaN).

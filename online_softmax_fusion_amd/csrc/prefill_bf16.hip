@@ -104,13 +104,17 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     // every row's raw score: the A operand holds v_j = (slope / scale) (j -
     // P0) split into three bf16 parts (hi + mid + lo = v_j to fp32 precision)
     // in k = 0..2 of key row j, the B operand ones in k = 0..2.  P0 is the
-    // position of the workgroup's first row, which keeps v_j small for the
-    // keys near the rows' positions (the ones that carry the weight).
+    // position of the wave's first row, which keeps v_j small for the keys
+    // near the rows' positions (the ones that carry the weight): the fp32
+    // score then carries an error of about 2^-23 slope log2(e) |j - P0|, at
+    // most ~1e-4 (log2 units) over the keys with weight for slopes up to 64.
     // slope_l2 carries slope / scale for this kind.
     u32x4 ext_a[2], ext_b;
     if constexpr (AC) {
+        // qpos - wrow is the workgroup's first position; the wave's is 32 wv past it
         const int wrow = ((int)threadIdx.x >> 6) * 32 + (lane & 31);   // the row's index in the workgroup
-        const int jrel = kt0 + perm32(lane & 31) - (qpos - wrow);       // key of A row r minus P0
+        const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const int jrel = kt0 + perm32(lane & 31) - (qpos - wrow) - 32 * wv;   // key of A row r minus P0
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const float v = slope_l2 * (float)(jrel + kb * 32);
@@ -540,7 +544,7 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
             if (hh == 0) {
                 float mp = (m_run == -INFINITY) ? -INFINITY : m_run * kLn2;
                 // the folded ALiBi's row constant, as in the LSE of the plain prefill
-                if constexpr (BIAS == kBiasAlibiCausal) mp -= p.slopes[h] * (float)(qrow - q0);
+                if constexpr (BIAS == kBiasAlibiCausal) mp -= p.slopes[h] * (float)r;
                 p.m_part[prow] = mp;
                 p.l_part[prow] = l_tot;
             }
@@ -568,8 +572,9 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
         }
         if (p.lse != nullptr && hh == 0) {
             float lse = (l_tot > 0.f) ? m_run * kLn2 + logf(l_tot) : -INFINITY;
-            // the row constant of the folded ALiBi bias: slope (pos - P0), P0 = q0 + Lk - Lq
-            if constexpr (BIAS == kBiasAlibiCausal) lse -= p.slopes[h] * (float)(qrow - q0);
+            // the row constant of the folded ALiBi bias: slope (pos - P0), P0 the position
+            // of the wave's first row
+            if constexpr (BIAS == kBiasAlibiCausal) lse -= p.slopes[h] * (float)r;
             p.lse[((int64_t)b * p.Hq + h) * p.Lq + qrow] = lse;
         }
     }

@@ -330,6 +330,54 @@ def test_alibi_matches_dense_bias_of_its_values(causal, Lq, Lk):
     assert float((l_0[fin] - l_n[fin]).abs().max()) <= 1e-3
 
 
+# Slopes beyond ALiBi's own (which are at most 1), of both signs.  Under a
+# causal mask the bias is folded into the key-query product relative to the
+# position of each wave's first row, so the rounding it adds grows with the
+# slope; up to |slope| = 64 it stays inside the bf16 bars.  Checked in the
+# four-wave and eight-wave workgroups (the correction of each wave's row
+# constant) and in the split form (the per-chunk reference values).
+SLOPE_RANGE = [0.5, 8.0, 64.0, -0.05]
+
+
+def _slopes(Hq):
+    return torch.tensor([SLOPE_RANGE[h % len(SLOPE_RANGE)] for h in range(Hq)], dtype=torch.float32)
+
+
+def test_folded_alibi_slope_range_four_waves():
+    w, q, k, v, _, _ = inputs(1, 4, 4, 300, 330, 128, "bf16", True, "alibi", seed=61)
+    sl = _slopes(4)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), True, alibi_slopes=sl.cuda())
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True, alibi_slopes=sl)
+    compare(o, lse, O_ref, L_ref, "bf16", "slopes %s" % SLOPE_RANGE)
+
+
+def test_folded_alibi_slope_range_split():
+    w, q, k, v, _, _ = inputs(1, 4, 4, 200, 1500, 128, "bf16", True, "alibi", seed=62)
+    sl = _slopes(4)
+    op, mp, lp = attn.attn_fwd_prefill_splitk(q.cuda(), k.cuda(), v.cuda(), 3, w.softmax_scale(), True,
+                                              alibi_slopes=sl.cuda())
+    o, lse = attn.attn_splitk_combine(op, mp, lp, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True, alibi_slopes=sl)
+    compare(o, lse, O_ref, L_ref, "bf16", "split, slopes %s" % SLOPE_RANGE)
+
+
+def test_folded_alibi_slope_range_eight_waves():
+    B, Hq, Hkv, Lq, Lk = 1, 64, 8, 1030, 8900   # eight-wave workgroups (as in the sampled cases above)
+    w = synth.Workload("case8", B, Hq, Hkv, Lq, Lk, 128, "bf16", True, "alibi", 63)
+    q, k, v = synth.make_qkv(w)
+    sl = _slopes(Hq)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), True, alibi_slopes=sl.cuda())
+    torch.cuda.synchronize()
+    # the first rows of all eight waves of the first and last 256-row blocks, their neighbours
+    local = sorted({i for t in (0, 768, 1024) for i in range(t, min(t + 256, Lq), 31)} | {Lq - 1})
+    rows = np.array([h * Lq + i for h in range(Hq) for i in local], dtype=np.int64)
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True, rows=rows, alibi_slopes=sl)
+    idx = torch.from_numpy(rows).cuda()
+    compare(o.reshape(-1, 128)[idx], lse.reshape(-1)[idx], O_ref, L_ref, "bf16", "eight waves, slopes")
+
+
 def test_prefill_deterministic():
     w, q, k, v, _, _ = inputs(1, 4, 4, 300, 300, 128, "bf16", True, "alibi", seed=4)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
