@@ -50,6 +50,7 @@ namespace attn {
 namespace {
 
 constexpr float kTau = 8.0f;
+constexpr float kTauPow = 256.0f;   // 2^kTau
 
 template <int D>
 struct TileCfg {
@@ -129,32 +130,37 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     }
 
     // 1. S^T = K Q^T, the two 32-key blocks interleaved (two accumulation
-    //    chains); the K operand reads run ahead of the matrix core (below)
+    //    chains); the K operand reads run ahead of the matrix core (below).
+    //    A lambda: the rare path of step 3 recomputes the scores from the K
+    //    tile, which is still in LDS, rather than keeping them live.
     f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    auto qk = [&]() {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-            s[kb] = mfma32(as_bf16x8(load16(lk + ((kbase ^ (ks << 5)) + kb * 32 * C::RB))), as_bf16x8(qreg[ks]), s[kb]);
-    // schedule: operand reads ahead of the matrix core. For D = 128 two reads in flight ahead of
-    // each product measured fastest (1 to 2% over 4, 6, 8 or 12; 1 spills); for D = 64 the
-    // choice made no measurable difference and all eight are issued up front.
-    constexpr int RA = C::KS == 8 ? 2 : 2 * C::KS;
-    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * C::KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 2 * C::KS - RA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (AC) {
+            for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(as_bf16x8(ext_a[kb]), as_bf16x8(ext_b), s[kb]);
-    }
-    // 2. score modifier; tile max (raw scores when the scale is folded)
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                s[kb] = mfma32(as_bf16x8(load16(lk + ((kbase ^ (ks << 5)) + kb * 32 * C::RB))), as_bf16x8(qreg[ks]), s[kb]);
+        // schedule: operand reads ahead of the matrix core. For D = 128 two reads in flight ahead of
+        // each product measured fastest (1 to 2% over 4, 6, 8 or 12; 1 spills); for D = 64 the
+        // choice made no measurable difference and all eight are issued up front.
+        constexpr int RA = C::KS == 8 ? 2 : 2 * C::KS;
+        __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < 2 * C::KS - RA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (AC) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(as_bf16x8(ext_a[kb]), as_bf16x8(ext_b), s[kb]);
+        }
+    };
+
+    // 2. score modifier
     const float sc = p.scale_log2;
     // tiled dense bias: this lane's values come 8 consecutive keys (one
     // 16-byte chunk of its row) at a time; element e of block kb is key
@@ -171,56 +177,88 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     u32x4 bch{};
     // ALiBi distance qpos - j = dbase - (a compile-time offset of the element)
     const float dbase = (float)(qpos - kt0 - hh * 8);
-    float mx = -INFINITY;
+    // the score modifier in place (log2 units unless the scale is folded),
+    // masked keys set to -inf; returns this lane's maximum
+    auto modify = [&]() {
+        float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int j = kt0 + kb * 32 + (e >> 3) * 16 + hh * 8 + (e & 7);
-            if (BK == kBiasDenseBf16Tiled && (e & 7) == 0)
-                bch = load16(lb + (bbase ^ ((4 * kb + 2 * (e >> 3) + hh) << 4)));
-            float x = s[kb][e];
-            if (!FOLD) {
-                x *= sc;
-                if (CAP) {   // in log2 units
-                    if constexpr (BIAS == kBiasNoneCapExp)
-                        x = soft_cap_exp(x, p.cap_l2, p.cap_k);
-                    else
-                        x = soft_cap(x, p.cap_l2, p.cap_k, p.cap_inv);
+            for (int e = 0; e < 16; ++e) {
+                const int j = kt0 + kb * 32 + (e >> 3) * 16 + hh * 8 + (e & 7);
+                if (BK == kBiasDenseBf16Tiled && (e & 7) == 0)
+                    bch = load16(lb + (bbase ^ ((4 * kb + 2 * (e >> 3) + hh) << 4)));
+                float x = s[kb][e];
+                if (!FOLD) {
+                    x *= sc;
+                    if (CAP) {   // in log2 units
+                        if constexpr (BIAS == kBiasNoneCapExp)
+                            x = soft_cap_exp(x, p.cap_l2, p.cap_k);
+                        else
+                            x = soft_cap(x, p.cap_l2, p.cap_k, p.cap_inv);
+                    }
+                    if (BK == kBiasAlibi) {
+                        x = fmaf(-slope_l2, fabsf(dbase - (float)(kb * 32 + (e >> 3) * 16 + (e & 7))), x);
+                    } else if (BK == kBiasDenseBf16Tiled) {
+                        const uint32_t wv = bch[(e & 7) >> 1];
+                        const float bv = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+                        x = fmaf(bv, kLog2e, x);
+                    } else if (BK == kBiasDenseF32 || BK == kBiasDenseBf16) {
+                        const int bi = min(qrow, p.Lq - 1);
+                        const int bj = min(j, p.Lk - 1);
+                        const int64_t idx = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
+                                            (int64_t)bi * p.bias_si + (int64_t)bj * p.bias_sj;
+                        float bv;
+                        if (BK == kBiasDenseF32)
+                            bv = static_cast<const float *>(p.bias)[idx];
+                        else
+                            bv = bf16_bits_to_f32(static_cast<const uint16_t *>(p.bias)[idx]);
+                        x = fmaf(bv, kLog2e, x);
+                    }
                 }
-                if (BK == kBiasAlibi) {
-                    x = fmaf(-slope_l2, fabsf(dbase - (float)(kb * 32 + (e >> 3) * 16 + (e & 7))), x);
-                } else if (BK == kBiasDenseBf16Tiled) {
-                    const uint32_t wv = bch[(e & 7) >> 1];
-                    const float bv = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
-                    x = fmaf(bv, kLog2e, x);
-                } else if (BK == kBiasDenseF32 || BK == kBiasDenseBf16) {
-                    const int bi = min(qrow, p.Lq - 1);
-                    const int bj = min(j, p.Lk - 1);
-                    const int64_t idx = (int64_t)b * p.bias_sb + (int64_t)h * p.bias_sh +
-                                        (int64_t)bi * p.bias_si + (int64_t)bj * p.bias_sj;
-                    float bv;
-                    if (BK == kBiasDenseF32)
-                        bv = static_cast<const float *>(p.bias)[idx];
-                    else
-                        bv = bf16_bits_to_f32(static_cast<const uint16_t *>(p.bias)[idx]);
-                    x = fmaf(bv, kLog2e, x);
-                }
+                if (MASK && (j < jmin || j > jmax)) x = -INFINITY;
+                s[kb][e] = x;
+                mx = fmaxf(mx, x);
             }
-            if (MASK && (j < jmin || j > jmax)) x = -INFINITY;
-            s[kb][e] = x;
-            mx = fmaxf(mx, x);
         }
-    }
-    mx = xor32_max(mx);
-    if (FOLD) mx *= sc;   // sc > 0: max commutes with the scaling
-    if constexpr (CE) {
-        if (mx != -INFINITY) mx = soft_cap_exp(mx, p.cap_l2, p.cap_k);
-    }
+        return mx;
+    };
 
-    // 3. lazy repair of l and O when the max has grown by more than TAU
-    if (__any(mx > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mx);
+    // weights P = 2^(t - m_use) in fp32, packed to bf16; returns this lane's sum
+    uint32_t pk[2][8];
+    auto weights = [&](float m_use) {
+        float lt = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                float p0, p1;
+                if constexpr (CE) {
+                    // capped - m = (c - m) - 2c / (2^(s * sc * k2) + 1); a masked score
+                    // (-inf) would give 2^(-c - m), so it is zeroed explicitly
+                    const float cm = p.cap_l2 - m_use, c2 = -2.f * p.cap_l2, u = sc * p.cap_k;
+                    p0 = exp2_fast(fmaf(c2, __builtin_amdgcn_rcpf(exp2_fast(s[kb][e] * u) + 1.f), cm));
+                    p1 = exp2_fast(fmaf(c2, __builtin_amdgcn_rcpf(exp2_fast(s[kb][e + 1] * u) + 1.f), cm));
+                    if (MASK) {
+                        if (s[kb][e] == -INFINITY) p0 = 0.f;
+                        if (s[kb][e + 1] == -INFINITY) p1 = 0.f;
+                    }
+                } else if (FOLD) {
+                    p0 = exp2_fast(fmaf(s[kb][e], sc, -m_use));
+                    p1 = exp2_fast(fmaf(s[kb][e + 1], sc, -m_use));
+                } else {
+                    p0 = exp2_fast(s[kb][e] - m_use);
+                    p1 = exp2_fast(s[kb][e + 1] - m_use);
+                }
+                lt += p0 + p1;
+                pk[kb][e >> 1] = pack_bf16x2(p0, p1);
+            }
+        }
+        return lt;
+    };
+
+    // lazy repair of l and O to the reference m_new (per lane; m_new >= m_run)
+    auto repair = [&](float m_new) {
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
         l_run *= alpha;
         // in place, so the accumulators keep their registers across this rarely
@@ -230,36 +268,47 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
 #pragma unroll
             for (int e = 0; e < 16; ++e) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(oacc[db][e]) : "v"(alpha));
         m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    };
 
-    // 4. P = 2^(t - m) in fp32, summed in fp32, packed to bf16
-    uint32_t pk[2][8];
+    qk();
+    if constexpr (BIAS == kBiasNone) {
+        // 3./4. Without a score modifier the weights are formed against the
+        // running reference m_run without the tile's maximum.  If every weight of the wave is at
+        // most 2^TAU (checked through this lane's sum, whose terms are >= 0)
+        // they are kept: the reference may trail the true maximum by up to
+        // TAU, as with the lazy repair.  Otherwise (the first tile, where
+        // m_run = -inf gives inf or NaN weights, or a maximum that grew by
+        // more than TAU) the tile's maximum is taken, l and O are repaired to
+        // it when it grew, and the weights are formed again.  (With the folded
+        // ALiBi bias the maximum grows by slope * 64 keys per tile, so the
+        // other kinds take the maximum first.)
+        if constexpr (MASK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-            float p0, p1;
-            if constexpr (CE) {
-                // capped - m = (c - m) - 2c / (2^(s * sc * k2) + 1); a masked score
-                // (-inf) would give 2^(-c - m), so it is zeroed explicitly
-                const float cm = p.cap_l2 - m_use, c2 = -2.f * p.cap_l2, u = sc * p.cap_k;
-                p0 = exp2_fast(fmaf(c2, __builtin_amdgcn_rcpf(exp2_fast(s[kb][e] * u) + 1.f), cm));
-                p1 = exp2_fast(fmaf(c2, __builtin_amdgcn_rcpf(exp2_fast(s[kb][e + 1] * u) + 1.f), cm));
-                if (MASK) {
-                    if (s[kb][e] == -INFINITY) p0 = 0.f;
-                    if (s[kb][e + 1] == -INFINITY) p1 = 0.f;
+                for (int e = 0; e < 16; ++e) {
+                    const int j = kt0 + kb * 32 + (e >> 3) * 16 + hh * 8 + (e & 7);
+                    if (j < jmin || j > jmax) s[kb][e] = -INFINITY;
                 }
-            } else if (FOLD) {
-                p0 = exp2_fast(fmaf(s[kb][e], sc, -m_use));
-                p1 = exp2_fast(fmaf(s[kb][e + 1], sc, -m_use));
-            } else {
-                p0 = exp2_fast(s[kb][e] - m_use);
-                p1 = exp2_fast(s[kb][e + 1] - m_use);
-            }
-            l_run += p0 + p1;
-            pk[kb][e >> 1] = pack_bf16x2(p0, p1);
         }
+        float lt = weights(m_run);
+        if (__any(!(lt <= kTauPow))) {
+            qk();
+            const float mx = xor32_max(modify()) * sc;   // sc > 0: max commutes with the scaling
+            if (__any(mx > m_run)) repair(fmaxf(m_run, mx));
+            lt = weights((m_run == -INFINITY) ? 0.f : m_run);
+        }
+        l_run += lt;
+    } else {
+        float mx = xor32_max(modify());
+        if (FOLD) mx *= sc;   // sc > 0: max commutes with the scaling
+        if constexpr (CE) {
+            if (mx != -INFINITY) mx = soft_cap_exp(mx, p.cap_l2, p.cap_k);
+        }
+        // 3. lazy repair of l and O when the max has grown by more than TAU
+        if (__any(mx > m_run + kTau)) repair(fmaxf(m_run, mx));
+        // 4. P = 2^(t - m) in fp32, summed in fp32, packed to bf16
+        l_run += weights((m_run == -INFINITY) ? 0.f : m_run);
     }
 
     // 5. O^T += V^T P^T: A operand = 8 keys of one d per lane, by two
@@ -478,33 +527,40 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     float l_run = 0.f;         // running sum over this lane's half of the keys
 
 
-    if (t_end > t_first) {
-        ATTN_ISSUE_TILE_LOADS(t_first, lds_k0, lds_v0, lds_b0);
-        wait_vmem();
-        __syncthreads();
-    }
-
-    // Tile t sits in buffer (t - t_first) & 1.  Masked tiles (the window's
+    // Visiting order.  Keys ascend, except with the folded causal ALiBi
+    // bias: its scores grow with the key (the bias is largest at the row's own
+    // position), so ascending keys would raise the running maximum by about
+    // slope * 64 keys on every tile and repair l and O each time; descending
+    // from the diagonal, the first tile holds the largest biases and later
+    // tiles rarely move the maximum.  Step n handles tile t_end - 1 - n there.
+    // Step n's tile sits in LDS buffer n & 1.  Masked tiles (the window's
     // left edge, the causal diagonal band, the key tail) take the generic
     // step; the unmasked middle runs two tiles per trip so that each LDS
     // buffer's address is a constant.
+    constexpr bool REV = (BIAS == kBiasAlibiCausal);
+    if (t_end > t_first) {
+        ATTN_ISSUE_TILE_LOADS(REV ? t_end - 1 : t_first, lds_k0, lds_v0, lds_b0);
+        wait_vmem();
+        __syncthreads();
+    }
 #define ATTN_STEP(MASK_, BUF_, T_)                                                                               \
     tile_step<D, BIAS, MASK_>(p, (BUF_) ? lds_k1 : lds_k0, (BUF_) ? lds_v1 : lds_v0, (BUF_) ? lds_b1 : lds_b0,   \
                               kbase, vbase, qreg, oacc,                                                         \
                               m_run, l_run, (T_) * BC, wrow0, wjmin, wjmax, qrow, qpos, jmin, jmax, slope_l2, b, h, \
                               lane)
-#define ATTN_GENERIC_STEP(T_)                                                                                   \
+    // step N_ on tile T_, prefetching tile NEXT_ (if HAS_NEXT_) into the other buffer
+#define ATTN_GENERIC_STEP(N_, T_, HAS_NEXT_, NEXT_)                                                            \
     do {                                                                                                        \
         const int tg_ = (T_);                                                                                   \
         const bool masked_ = tg_ < u_first || tg_ >= u_end;                                                     \
-        if (((tg_ - t_first) & 1) == 0) {                                                                       \
-            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k1, lds_v1, lds_b1);                                \
+        if (((N_) & 1) == 0) {                                                                                  \
+            if (HAS_NEXT_) ATTN_ISSUE_TILE_LOADS(NEXT_, lds_k1, lds_v1, lds_b1);                                \
             if (masked_)                                                                                        \
                 ATTN_STEP(true, 0, tg_);                                                                        \
             else                                                                                                \
                 ATTN_STEP(false, 0, tg_);                                                                       \
         } else {                                                                                                \
-            if (tg_ + 1 < t_end) ATTN_ISSUE_TILE_LOADS(tg_ + 1, lds_k0, lds_v0, lds_b0);                                \
+            if (HAS_NEXT_) ATTN_ISSUE_TILE_LOADS(NEXT_, lds_k0, lds_v0, lds_b0);                                \
             if (masked_)                                                                                        \
                 ATTN_STEP(true, 1, tg_);                                                                        \
             else                                                                                                \
@@ -513,19 +569,41 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
         wait_vmem();                                                                                            \
         __syncthreads();                                                                                        \
     } while (0)
-    int t = t_first;
-    for (; t < t_end && !(t >= u_first && ((t - t_first) & 1) == 0); ++t) ATTN_GENERIC_STEP(t);
-    for (; t + 1 < u_end; t += 2) {
-        ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1, lds_b1);
-        ATTN_STEP(false, 0, t);
-        wait_vmem();
-        __syncthreads();
-        if (t + 2 < t_end) ATTN_ISSUE_TILE_LOADS(t + 2, lds_k0, lds_v0, lds_b0);
-        ATTN_STEP(false, 1, t + 1);
-        wait_vmem();
-        __syncthreads();
+    if constexpr (REV) {
+        // descending: step n on tile t_end - 1 - n; the unmasked steps are
+        // [t_end - u_end, t_end - u_first)
+        const int N = t_end - t_first, n_u0 = t_end - u_end, n_u1 = t_end - u_first;
+        int n = 0;
+        for (; n < N && !(n >= n_u0 && (n & 1) == 0); ++n)
+            ATTN_GENERIC_STEP(n, t_end - 1 - n, n + 1 < N, t_end - 2 - n);
+        for (; n + 1 < n_u1; n += 2) {
+            ATTN_ISSUE_TILE_LOADS(t_end - 2 - n, lds_k1, lds_v1, lds_b1);
+            ATTN_STEP(false, 0, t_end - 1 - n);
+            wait_vmem();
+            __syncthreads();
+            if (n + 2 < N) ATTN_ISSUE_TILE_LOADS(t_end - 3 - n, lds_k0, lds_v0, lds_b0);
+            ATTN_STEP(false, 1, t_end - 2 - n);
+            wait_vmem();
+            __syncthreads();
+        }
+        for (; n < N; ++n) ATTN_GENERIC_STEP(n, t_end - 1 - n, n + 1 < N, t_end - 2 - n);
+    } else {
+        // ascending: step t - t_first on tile t
+        int t = t_first;
+        for (; t < t_end && !(t >= u_first && ((t - t_first) & 1) == 0); ++t)
+            ATTN_GENERIC_STEP(t - t_first, t, t + 1 < t_end, t + 1);
+        for (; t + 1 < u_end; t += 2) {
+            ATTN_ISSUE_TILE_LOADS(t + 1, lds_k1, lds_v1, lds_b1);
+            ATTN_STEP(false, 0, t);
+            wait_vmem();
+            __syncthreads();
+            if (t + 2 < t_end) ATTN_ISSUE_TILE_LOADS(t + 2, lds_k0, lds_v0, lds_b0);
+            ATTN_STEP(false, 1, t + 1);
+            wait_vmem();
+            __syncthreads();
+        }
+        for (; t < t_end; ++t) ATTN_GENERIC_STEP(t - t_first, t, t + 1 < t_end, t + 1);
     }
-    for (; t < t_end; ++t) ATTN_GENERIC_STEP(t);
 #undef ATTN_GENERIC_STEP
 #undef ATTN_STEP
 
