@@ -779,7 +779,7 @@ def traffic_table(d):
          ""),
         ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 10, true>"), w3, PREFILL_SOURCES, pf(w3), pgrid(w3),
          ""),
-        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 8, 9, true>",), w3d, PREFILL_SOURCES,
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 8, 12, true>",), w3d, PREFILL_SOURCES,
          pf(w3d) + dense_bias_bytes(w3d), pgrid(w3d), ""),
         ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 0, true>"), w5, PREFILL_SOURCES, pf(w5), pgrid(w5),
          ""),

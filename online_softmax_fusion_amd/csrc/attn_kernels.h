@@ -9,24 +9,28 @@ namespace attn {
 
 // kBiasNoneScaled: no bias, score formed explicitly (used when the scale is not
 // positive).  The *Cap kinds add the soft cap of the scaled score.
-// Two kinds are chosen by the prefill launcher and never set by the host
+// Four kinds are chosen by the prefill launcher and never set by the host
 // interface: kBiasDenseBf16Tiled, a bf16 dense bias whose rows are contiguous
-// and 16-byte aligned, loaded a tile at a time into LDS beside K and V; and
-// kBiasAlibiCausal, ALiBi under a causal mask with a positive scale, whose
-// bias is added to the scores by one more matrix-core product; and
-// kBiasNoneCapExp, the soft cap without a bias for caps up to 64, formed by
-// the exp form alone (soft_cap_exp).
+// and 16-byte aligned, loaded a tile at a time into LDS beside K and V, and
+// kBiasDenseBf16TiledDesc, the same under a causal mask with the key tiles
+// visited from the diagonal down; kBiasAlibiCausal, ALiBi under a causal mask
+// with a positive scale, whose bias is added to the scores by one more
+// matrix-core product; and kBiasNoneCapExp, the soft cap without a bias for
+// caps up to 64, formed by the exp form alone (soft_cap_exp).
 enum BiasKind {
     kBiasNone = 0, kBiasAlibi = 1, kBiasDenseF32 = 2, kBiasDenseBf16 = 3, kBiasNoneScaled = 4,
     kBiasNoneCap = 5, kBiasAlibiCap = 6, kBiasDenseF32Cap = 7, kBiasDenseBf16Cap = 8,
-    kBiasDenseBf16Tiled = 9, kBiasAlibiCausal = 10, kBiasNoneCapExp = 11
+    kBiasDenseBf16Tiled = 9, kBiasAlibiCausal = 10, kBiasNoneCapExp = 11, kBiasDenseBf16TiledDesc = 12
 };
 // whether a kind carries the soft cap, and its bias part
 constexpr bool bias_cap(int kind) {
     return (kind >= kBiasNoneCap && kind <= kBiasDenseBf16Cap) || kind == kBiasNoneCapExp;
 }
 constexpr int bias_base(int kind) {
-    return (kind == kBiasNoneCap || kind == kBiasNoneCapExp) ? kBiasNoneScaled : bias_cap(kind) ? kind - 5 : kind;
+    return (kind == kBiasNoneCap || kind == kBiasNoneCapExp) ? kBiasNoneScaled
+           : kind == kBiasDenseBf16TiledDesc                  ? kBiasDenseBf16Tiled
+           : bias_cap(kind)                                   ? kind - 5
+                                                              : kind;
 }
 
 // One attention problem after validation.  Strides are in elements.

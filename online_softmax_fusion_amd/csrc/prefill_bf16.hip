@@ -403,7 +403,7 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     __shared__ __attribute__((aligned(1024))) char lds_v0[C::TILE];
     __shared__ __attribute__((aligned(1024))) char lds_v1[C::TILE];
     // tiled dense bias: the workgroup's BR rows x 64 keys of bf16 per tile
-    constexpr bool TB = (BIAS == kBiasDenseBf16Tiled);
+    constexpr bool TB = (bias_base(BIAS) == kBiasDenseBf16Tiled);
     constexpr int BTILE = TB ? BR * BC * 2 : 16;
     constexpr int NB = BTILE / (T * 16);     // 16-byte direct loads per thread per bias tile
     static_assert(!TB || NB * T * 16 == BTILE, "bias tile does not split evenly");
@@ -527,17 +527,22 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     float l_run = 0.f;         // running sum over this lane's half of the keys
 
 
-    // Visiting order.  Keys ascend, except with the folded causal ALiBi
-    // bias: its scores grow with the key (the bias is largest at the row's own
-    // position), so ascending keys would raise the running maximum by about
-    // slope * 64 keys on every tile and repair l and O each time; descending
-    // from the diagonal, the first tile holds the largest biases and later
-    // tiles rarely move the maximum.  Step n handles tile t_end - 1 - n there.
+    // Visiting order.  Keys ascend (a head's query tiles then start on the
+    // same K/V tiles, which stay in L2), except with the folded causal ALiBi
+    // bias and the tiled dense bias.  The folded bias makes the scores grow
+    // with the key (it is largest at the row's own position), so ascending
+    // keys would raise the running maximum by about slope * 64 keys on every
+    // tile and repair l and O each time; descending from the diagonal, the
+    // first tile holds the largest biases and later tiles rarely move the
+    // maximum.  Under a causal mask dense position biases mostly share that
+    // shape (largest near the diagonal), so the tiled dense bias descends
+    // too there (kBiasDenseBf16TiledDesc); a bias without it pays the L2
+    // effect instead (1-2%).  Step n handles tile t_end - 1 - n there.
     // Step n's tile sits in LDS buffer n & 1.  Masked tiles (the window's
     // left edge, the causal diagonal band, the key tail) take the generic
     // step; the unmasked middle runs two tiles per trip so that each LDS
     // buffer's address is a constant.
-    constexpr bool REV = (BIAS == kBiasAlibiCausal);
+    constexpr bool REV = (BIAS == kBiasAlibiCausal) || (BIAS == kBiasDenseBf16TiledDesc);
     if (t_end > t_first) {
         ATTN_ISSUE_TILE_LOADS(REV ? t_end - 1 : t_first, lds_k0, lds_v0, lds_b0);
         wait_vmem();
@@ -570,23 +575,21 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
         __syncthreads();                                                                                        \
     } while (0)
     if constexpr (REV) {
-        // descending: step n on tile t_end - 1 - n; the unmasked steps are
-        // [t_end - u_end, t_end - u_first)
-        const int N = t_end - t_first, n_u0 = t_end - u_end, n_u1 = t_end - u_first;
-        int n = 0;
-        for (; n < N && !(n >= n_u0 && (n & 1) == 0); ++n)
-            ATTN_GENERIC_STEP(n, t_end - 1 - n, n + 1 < N, t_end - 2 - n);
-        for (; n + 1 < n_u1; n += 2) {
-            ATTN_ISSUE_TILE_LOADS(t_end - 2 - n, lds_k1, lds_v1, lds_b1);
-            ATTN_STEP(false, 0, t_end - 1 - n);
+        // descending: tile t is step t_end - 1 - t
+        int t = t_end - 1;
+        for (; t >= t_first && !(t < u_end && ((t_end - 1 - t) & 1) == 0); --t)
+            ATTN_GENERIC_STEP(t_end - 1 - t, t, t > t_first, t - 1);
+        for (; t - 1 >= u_first; t -= 2) {
+            ATTN_ISSUE_TILE_LOADS(t - 1, lds_k1, lds_v1, lds_b1);
+            ATTN_STEP(false, 0, t);
             wait_vmem();
             __syncthreads();
-            if (n + 2 < N) ATTN_ISSUE_TILE_LOADS(t_end - 3 - n, lds_k0, lds_v0, lds_b0);
-            ATTN_STEP(false, 1, t_end - 2 - n);
+            if (t - 2 >= t_first) ATTN_ISSUE_TILE_LOADS(t - 2, lds_k0, lds_v0, lds_b0);
+            ATTN_STEP(false, 1, t - 1);
             wait_vmem();
             __syncthreads();
         }
-        for (; n < N; ++n) ATTN_GENERIC_STEP(n, t_end - 1 - n, n + 1 < N, t_end - 2 - n);
+        for (; t >= t_first; --t) ATTN_GENERIC_STEP(t_end - 1 - t, t, t > t_first, t - 1);
     } else {
         // ascending: step t - t_first on tile t
         int t = t_first;
@@ -769,6 +772,9 @@ hipError_t launch_prefill_k(const FwdParams &p, int kind, hipStream_t stream) {
         case kBiasDenseBf16Tiled:
             if constexpr (D == 128 && NW == 8) return launch_prefill_t<D, NW, kBiasDenseBf16Tiled>(p, stream);
             return hipErrorInvalidValue;
+        case kBiasDenseBf16TiledDesc:
+            if constexpr (D == 128 && NW == 8) return launch_prefill_t<D, NW, kBiasDenseBf16TiledDesc>(p, stream);
+            return hipErrorInvalidValue;
         case kBiasAlibiCausal: return launch_prefill_t<D, NW, kBiasAlibiCausal>(p, stream);
         case kBiasNone: return launch_prefill_t<D, NW, kBiasNone>(p, stream);
         case kBiasNoneScaled: return launch_prefill_t<D, NW, kBiasNoneScaled>(p, stream);
@@ -802,9 +808,9 @@ hipError_t launch_prefill_d(const FwdParams &p, hipStream_t stream) {
     if (D == 128 && kind == kBiasDenseBf16 && bias_tiles_fit(p)) {
         // the bias tile takes LDS beside K and V: one 8-wave workgroup per CU
         FwdParams pt = p;
-        pt.bias_kind = kBiasDenseBf16Tiled;
+        pt.bias_kind = p.causal ? kBiasDenseBf16TiledDesc : kBiasDenseBf16Tiled;
         pt.bias_plane_bytes = (uint32_t)(((int64_t)p.Lq - 1) * p.bias_si + p.Lk) * 2u;
-        return launch_prefill_k<D, 8>(pt, kBiasDenseBf16Tiled, stream);
+        return launch_prefill_k<D, 8>(pt, pt.bias_kind, stream);
     }
     if (D == 128 && prefill_waves(p) == 8) return launch_prefill_k<D, 8>(p, kind, stream);
     return launch_prefill_k<D, 4>(p, kind, stream);
