@@ -198,6 +198,8 @@ MOD_CASES = [
     (1, 2, 2, 150, 333, 128, "f32", True, "none", 4.0, (60, -1)),      # fp32 path
     (1, 2, 2, 97, 200, 64, "f32", False, "alibi", 1.5, (10, 10)),
     (1, 4, 4, 300, 420, 128, "bf16", True, "alibi", 0.0, (90, -1)),    # causal ALiBi + window (folded form)
+    (1, 4, 4, 300, 320, 128, "bf16", True, "dense_bf16", 0.0, (90, -1)),  # bias tiles, keys descending
+    (1, 2, 2, 260, 264, 128, "bf16", False, "dense_bf16", 0.0, (70, 30)),  # bias tiles, keys ascending
     (1, 4, 4, 300, 300, 128, "bf16", True, "none", 64.0, None),        # largest cap of the exp-only form
     (1, 4, 4, 300, 300, 128, "bf16", True, "none", 64.5, None),        # smallest cap of the exact form
 ]
@@ -376,6 +378,30 @@ def test_folded_alibi_slope_range_eight_waves():
     O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True, rows=rows, alibi_slopes=sl)
     idx = torch.from_numpy(rows).cuda()
     compare(o.reshape(-1, 128)[idx], lse.reshape(-1)[idx], O_ref, L_ref, "bf16", "eight waves, slopes")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("growth", [0.15, -0.15, 0.01])
+def test_prefill_running_max_growth(causal, growth):
+    """Scores that move steadily along the keys: s_ij ~ growth * j (natural
+    units) for every row.  Rising by ~9.6 per 64-key tile, the running maximum
+    outgrows the lazy threshold on every tile (the weights are re-formed after
+    a repair); falling, only the first tile sets it; rising slowly, the weights
+    of a tile sum past 2^8 without any single one passing it."""
+    B, H, Lq, Lk, D = 1, 2, 130, 520, 128
+    g = torch.Generator().manual_seed(71)
+    q0 = torch.randn(H, 1, D, generator=g)
+    q = (q0 + 0.01 * torch.randn(H, Lq, D, generator=g)).unsqueeze(0)
+    scale = 1.0 / math.sqrt(D)
+    unit = q0 / (q0.pow(2).sum(-1, keepdim=True) * scale)        # <q0, unit> * scale = 1
+    j = torch.arange(Lk, dtype=torch.float32).view(1, Lk, 1)
+    k = (growth * j * unit + 0.05 * torch.randn(H, Lk, D, generator=g)).unsqueeze(0)
+    v = torch.randn(B, H, Lk, D, generator=g)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), scale, causal)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, scale, causal)
+    compare(o, lse, O_ref, L_ref, "bf16", "growth %g causal %s" % (growth, causal))
 
 
 def test_prefill_deterministic():
