@@ -23,7 +23,9 @@
 //      2^(m_old - m_new).  The repair is taken lazily: it runs only when some
 //      row's max has grown by more than TAU = 8 (a factor 256), which keeps
 //      every exponent <= 2^8 and is exact in real arithmetic because the final
-//      normalisation uses the same reference m.
+//      normalisation uses the same reference m.  Without a score modifier the
+//      tile max is formed only when needed: the weights of step 4 are taken
+//      against the running m first and kept if none exceeds 2^8.
 //   4. P = 2^(t - m) in fp32; the row sum l accumulates the fp32 values (each
 //      lane keeps a partial over its half of the keys; the halves are added
 //      once at the end); P is packed to bf16 in registers.
@@ -39,8 +41,10 @@
 // tile.  Buffer loads carry the key range in their descriptor, so rows past
 // the end of K/V read as zero without any branch.  Causal tiles above the
 // diagonal are never loaded; a wave whose rows are all above a tile's keys
-// skips its matrix work.  Workgroups are ordered so that each XCD (which has
-// its own L2) works through whole heads, heaviest query tiles first.
+// skips its matrix work.  Key tiles ascend, except for the causal biases that
+// peak at the diagonal (folded ALiBi, tiled dense bias), which descend from
+// it.  Workgroups are ordered so that each XCD (which has its own L2) works
+// through whole heads, heaviest query tiles first.
 // Epilogue: O = O / l, LSE = m ln 2 + ln l; a row with no visible key gets
 // O = 0 and LSE = -inf.
 #include "attn_device.h"
