@@ -372,8 +372,11 @@ def time_prefill(w, steps, warmup, warm_s=1.0):
 
 
 def time_decode(w, steps, warmup, warm_s=1.0):
-    """Decode step = split-K local step + combine, issued eagerly; the kernel
-    time comes from HIP events around the local step."""
+    """Decode step = split-K local step + combine, issued eagerly.  The kernel
+    time comes from HIP events around the local step, timed over K launches of
+    the local step alone issued back to back: at batch 1 the eager two-call
+    step is bound by the host's launch work, and a kernel that starts after
+    the GPU has idled runs slower than in steady use."""
     import torch
     import synth
     import online_softmax_fusion_amd as attn
@@ -393,25 +396,31 @@ def time_decode(w, steps, warmup, warm_s=1.0):
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
     scale = w.softmax_scale()
 
-    def step(i, evs=None):
+    def local(i, evs=None):
         kk, vv = kvs[i % copies]
         if evs:
             evs[0].record(torch.cuda.current_stream())
         attn.attn_fwd_decode_splitk(q, kk, vv, S, scale, w.causal, o_part=op, m_part=mp, l_part=lp)
         if evs:
             evs[1].record(torch.cuda.current_stream())
+
+    def step(i):
+        local(i)
         attn.attn_splitk_combine(op, mp, lp, out=o, lse=lse)
 
     torch.cuda.synchronize()
     clock = ClockSampler().start()
     n = warm_up(step, warmup, warm_s)
     log("decode: %d untimed warm-up steps" % n)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, ev[i])
+        step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        local(i, ev[i])
+    torch.cuda.synchronize()
     sclk = clock.stop()
     durs = sorted(a.elapsed_time(b) for a, b in ev)
     avg_ms = sum(durs) / len(durs)
