@@ -733,11 +733,14 @@ hipError_t launch_prefill_t(const FwdParams &p, hipStream_t stream) {
 // the two waves of a SIMD come from two independent workgroups) overlap the
 // vector-heavy phases of the two waves better and leave twice as many
 // workgroups for short or unbalanced (causal) rows.  Measured on MI355X
-// (d = 128): eight waves are 1-6% faster for rows that see 4096 or more keys
-// on average (causal 8192, 16384, 32768; non-causal 4096, 8192; ALiBi
-// causal 8192), and 4-19% slower below that (causal 2048, 4096), with the
-// soft cap (15%), and for a 4096-key sliding window (1%); with only 16 query
-// rows against 32768 keys they are 38% slower (seven of the eight waves idle).
+// (d = 128): eight waves are faster for causal rows that see 4096 or more
+// keys on average (1-6%: causal 8192, 16384, 32768; ALiBi causal 8192) and
+// for non-causal rows of 2048 keys or more (1.5-3% at 2048, 4% at 4096, 5%
+// at 8192); they are even at about 2048 keys for causal rows and at 1536
+// non-causal, and 3-6% slower below that (non-causal 1024; causal 2048,
+// whose rows see 1024 keys on average), with the soft cap (2%), and for a
+// 4096-key sliding window (1%); with only 16 query rows against 32768 keys
+// they are 38% slower (seven of the eight waves idle).
 // A grid of fewer 256-row workgroups than CUs leaves CUs idle that the
 // 128-row grid would use (B1 H8 Lq 2048 Lk 32768: 0.654 vs 0.483 ms), and
 // with one 256-row workgroup per CU the uneven causal tiles finish unevenly
@@ -748,7 +751,7 @@ int prefill_waves(const FwdParams &p) {
     if (p.D != 128 || bias_cap(p.bias_kind) || p.window) return 4;   // the rule was measured at d = 128
     if (p.Lq < 1024) return 4;   // few rows: most waves of a 256-row tile would idle (Lq = 16: 678 vs 490 us)
     const int64_t avg_keys = p.causal ? (int64_t)p.Lk - ((int64_t)p.Lq - 1) / 2 : (int64_t)p.Lk;
-    if (avg_keys < 4096) return 4;
+    if (avg_keys < (p.causal ? 4096 : 2048)) return 4;
     const int64_t blocks8 = (int64_t)p.B * p.Hq * (((int64_t)p.Lq + 255) / 256);
     if (blocks8 < cus) return 4;
     if (p.causal && blocks8 < 2 * cus && avg_keys < 8192) return 4;
