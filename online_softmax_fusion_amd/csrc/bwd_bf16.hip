@@ -433,11 +433,15 @@ __device__ __forceinline__ void dkdv_scores(const FwdParams &p, const f32x16 &s,
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
         float pr[2], du[2];
+        // with ALiBi the distances are formed pair by pair where they are used
+        // (not all sixteen ahead of the products, which costs registers)
+        float db = dbase;
+        if constexpr (bias_base(BIAS) == kBiasAlibi) asm volatile("" : "+v"(db));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int eo = ((e + u) >> 3) * 16 + ((e + u) & 7);
             du[u] = grad_of_score<BIAS>(p, s[e + u], dp[e + u], L[(e + u) >> 2][(e + u) & 3],
-                                        Dl[(e + u) >> 2][(e + u) & 3], slope_l2, fabsf(dbase + (float)eo),
+                                        Dl[(e + u) >> 2][(e + u) & 3], slope_l2, fabsf(db + (float)eo),
                                         dense_bias<BIAS>(p, b, h, ibase + eo, key), &pr[u]);
             if (MASK && (uint32_t)(eo - lo) > span) pr[u] = du[u] = 0.f;
         }
@@ -679,8 +683,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
         dma_tile<D, T>(static_cast<const uint16_t *>(bp.dout) + (int64_t)b * bp.do_sb + (int64_t)hq * bp.do_sh +
                            (int64_t)q0 * bp.do_sl, dl_bytes, nv, dst + C::TILE, wave, dgoff);
         const int64_t rw = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
-        if (wave == 0) dma4(rsrc_words(bp.lse_l2 + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE, lane * 4);
-        if (wave == 1) dma4(rsrc_words(bp.delta + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE + BQ * 4, lane * 4);
+        // the lane's byte offset, formed here from the lane id rather than held across the loop
+        const uint32_t l4 = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4u;
+        if (wave == 0) dma4(rsrc_words(bp.lse_l2 + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE, l4);
+        if (wave == 1) dma4(rsrc_words(bp.delta + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE + BQ * 4, l4);
     };
     auto step = [&](bool masked, int it, int st) {
         const int hi = it / nt;
@@ -836,8 +842,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdParams bp) {
         dma_tile<D, T>(static_cast<const uint16_t *>(bp.dout) + (int64_t)b * bp.do_sb + (int64_t)hq * bp.do_sh +
                            (int64_t)q0 * bp.do_sl, dl_bytes, nv, dst + C::TILE, wave, dgoff);
         const int64_t rw = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
-        if (wave == 0) dma4(rsrc_words(bp.lse_l2 + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE, lane * 4);
-        if (wave == 1) dma4(rsrc_words(bp.delta + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE + BQ * 4, lane * 4);
+        // the lane's byte offset, formed here from the lane id rather than held across the loop
+        const uint32_t l4 = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4u;
+        if (wave == 0) dma4(rsrc_words(bp.lse_l2 + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE, l4);
+        if (wave == 1) dma4(rsrc_words(bp.delta + rw, (uint32_t)nv * 4u), dst + 2 * C::TILE + BQ * 4, l4);
     };
     auto step = [&](bool masked, int it, int st) {
         const int hi = it / nt;
@@ -916,10 +924,9 @@ hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     if (kv_blocks > 0) {
-        // d = 128: the paired-wave form (128 keys per workgroup as well); with
-        // ALiBi its distance terms do not fit the 256 registers, and it keeps
-        // one wave per SIMD
-        if constexpr (D == 128 && bias_base(BIAS) != kBiasAlibi)
+        // d = 128: the paired-wave form (128 keys per workgroup as well), for
+        // every score modifier
+        if constexpr (D == 128)
             hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, BIAS>), dim3((unsigned)kv_blocks), dim3(512), 0, stream, p);
         else
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, BIAS>), dim3((unsigned)kv_blocks), dim3(NW * 64), 0, stream, p);

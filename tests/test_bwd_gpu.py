@@ -105,6 +105,8 @@ BWD_CASES = [
     (2, 4, 2, 130, 257, 64, False, "none", 0.0, None),          # GQA, Lq != Lk, D = 64
     (1, 4, 1, 96, 160, 128, True, "none", 0.0, None),           # G = 4, causal with Lq < Lk
     (1, 2, 2, 150, 150, 128, True, "alibi", 0.0, None),
+    (1, 4, 2, 170, 290, 128, False, "alibi", 0.0, None),       # paired dK/dV with ALiBi, keys on both sides
+    (1, 2, 2, 160, 200, 128, True, "alibi", 6.0, (50, -1)),    # ALiBi + cap + window, paired dK/dV
     (1, 2, 1, 100, 140, 64, False, "dense_inf", 0.0, None),     # -inf bias entries, a dead row
     (2, 2, 2, 96, 190, 128, False, "dense_bf16", 0.0, None),
     (1, 2, 2, 180, 180, 128, True, "none", 5.0, None),          # soft cap
