@@ -28,7 +28,10 @@
 //                    head of the group stream through LDS.  Per 32 query rows
 //                    and wave: S = Q K^T and dP = dO V^T (queries in perm32
 //                    order), P and dS in registers, dV^T += dO^T P and
-//                    dK^T += Q^T dS with dO and Q read transposed.
+//                    dK^T += Q^T dS with dO and Q read transposed.  At d = 128
+//                    bwd_dkdv_pair_kernel does this work instead, with the K/V
+//                    rows in LDS and pairs of waves splitting the query rows,
+//                    so that two waves fit on each SIMD.
 //
 // Both kernels read each streamed tile twice: as rows (16-byte reads along d)
 // and transposed (ds_read_b64_tr_b16 along the rows).  One XOR swizzle of the
