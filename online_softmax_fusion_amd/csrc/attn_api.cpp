@@ -126,6 +126,14 @@ FwdParams make_params(const attn_fwd_args *a) {
         p.cap_l2 = a->softcap * 1.4426950408889634f;
         p.cap_k = 2.f / a->softcap;
         p.cap_inv = 1.f / p.cap_l2;
+        // the polynomial form for raw scores s with |s scale / softcap| <= 1/2:
+        // capped (log2) = s scale_log2 P(k s^2), k = (scale / softcap)^2
+        if (a->scale > 0.f) {
+            const double k = ((double)a->scale / a->softcap) * ((double)a->scale / a->softcap);
+            double kp = 1.0;
+            for (int i = 0; i < 4; ++i, kp *= k) p.cap_q[i] = (float)((double)p.scale_log2 * attn::kTanhPoly[i] * kp);
+            p.cap_s0 = (float)(0.5 * a->softcap / a->scale);
+        }
     }
     p.window = a->window;
     p.win_left = a->window_left;

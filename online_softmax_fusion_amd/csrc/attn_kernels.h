@@ -33,6 +33,15 @@ constexpr int bias_base(int kind) {
                                                               : kind;
 }
 
+// tanh(y) = y * (c0 + c1 y^2 + c2 y^4 + c3 y^6) for |y| <= 1/2, to an
+// absolute error of 1.3e-7: a minimax fit (Lawson's iteration on
+// Chebyshev nodes) of tanh(y) / y as a cubic in y^2 against the absolute
+// error of the product, coefficients rounded to float.  The soft cap c
+// tanh(t / c) then carries at most c * 1.3e-7 of error, against the exact
+// exp form's two more transcendental instructions per score.
+constexpr float kTanhPoly[4] = {0.9999976754188538f, -0.33320656418800354f, 0.13145145773887634f,
+                                -0.04337248206138611f};
+
 // One attention problem after validation.  Strides are in elements.
 struct FwdParams {
     const void *q, *k, *v;
@@ -57,6 +66,9 @@ struct FwdParams {
     float cap_l2;                       // soft cap in log2 units (softcap * log2(e)); 0 = off
     float cap_k;                        // 2 / softcap: 2^(x * cap_k) = e^(2 x / cap_l2)
     float cap_inv;                      // 1 / cap_l2
+    float cap_q[4];                     // capped score (log2 units) = s * (q0 + q1 w + q2 w^2 + q3 w^3),
+                                        // w = s^2, for raw scores |s| <= cap_s0 (tanh_poly, scaled)
+    float cap_s0;                       // raw-score range of cap_q: 0.5 * softcap / scale
     int window;                         // 1: apply win_left / win_right
     int win_left, win_right;            // keys left / right of the query position; < 0 = unbounded
     int num_cus, num_xcds;              // compute units and XCDs of the launch device

@@ -261,6 +261,29 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
         return lt;
     };
 
+    // the same weights with the cap as a polynomial in the raw score (CE
+    // only, every raw score of the wave within |s| <= cap_s0): one
+    // transcendental per score instead of three
+    auto weights_poly = [&](float m_use) {
+        float lt = 0.f;
+        const float q0 = p.cap_q[0], q1 = p.cap_q[1], q2 = p.cap_q[2], q3 = p.cap_q[3];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const float s0 = s[kb][e], s1 = s[kb][e + 1];
+                const float w0 = s0 * s0, w1 = s1 * s1;
+                const float c0 = fmaf(fmaf(fmaf(q3, w0, q2), w0, q1), w0, q0);
+                const float c1 = fmaf(fmaf(fmaf(q3, w1, q2), w1, q1), w1, q0);
+                const float p0 = exp2_fast(fmaf(s0, c0, -m_use));
+                const float p1 = exp2_fast(fmaf(s1, c1, -m_use));
+                lt += p0 + p1;
+                pk[kb][e >> 1] = pack_bf16x2(p0, p1);
+            }
+        }
+        return lt;
+    };
+
     // lazy repair of l and O to the reference m_new (per lane; m_new >= m_run)
     auto repair = [&](float m_new) {
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
@@ -275,9 +298,10 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     };
 
     qk();
-    if constexpr (BIAS == kBiasNone) {
-        // 3./4. Without a score modifier the weights are formed against the
-        // running reference m_run without the tile's maximum.  If every weight of the wave is at
+    if constexpr (BIAS == kBiasNone || CE) {
+        // 3./4. Without a score modifier, or with the exp-form soft cap, the
+        // weights are formed against the running reference m_run without the
+        // tile's maximum.  If every weight of the wave is at
         // most 2^TAU (checked through this lane's sum, whose terms are >= 0)
         // they are kept: the reference may trail the true maximum by up to
         // TAU, as with the lazy repair.  Otherwise (the first tile, where
@@ -295,10 +319,23 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                     if (j < jmin || j > jmax) s[kb][e] = -INFINITY;
                 }
         }
-        float lt = weights(m_run);
+        float lt;
+        if constexpr (CE && !MASK) {
+            float amax = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(s[kb][e]));
+            lt = __any(amax > p.cap_s0) ? weights(m_run) : weights_poly(m_run);
+        } else {
+            lt = weights(m_run);
+        }
         if (__any(!(lt <= kTauPow))) {
             qk();
-            const float mx = xor32_max(modify()) * sc;   // sc > 0: max commutes with the scaling
+            float mx = xor32_max(modify()) * sc;   // sc > 0: max commutes with the scaling
+            if constexpr (CE) {   // and with the cap, which is increasing
+                if (mx != -INFINITY) mx = soft_cap_exp(mx, p.cap_l2, p.cap_k);
+            }
             if (__any(mx > m_run)) repair(fmaxf(m_run, mx));
             lt = weights((m_run == -INFINITY) ? 0.f : m_run);
         }
@@ -306,9 +343,6 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     } else {
         float mx = xor32_max(modify());
         if (FOLD) mx *= sc;   // sc > 0: max commutes with the scaling
-        if constexpr (CE) {
-            if (mx != -INFINITY) mx = soft_cap_exp(mx, p.cap_l2, p.cap_k);
-        }
         // 3. lazy repair of l and O when the max has grown by more than TAU
         if (__any(mx > m_run + kTau)) repair(fmaxf(m_run, mx));
         // 4. P = 2^(t - m) in fp32, summed in fp32, packed to bf16

@@ -237,6 +237,25 @@ def test_decode_softcap_window_parity(case):
     compare(o, lse, O_ref, L_ref, dtype, str(case))
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("cap", [10.0, 50.0])
+def test_prefill_softcap_polynomial_and_exact_tiles(causal, cap):
+    """The prefill kernel forms the soft cap as a polynomial on key tiles whose
+    raw scores all lie within |scale s| <= cap / 2 and by the exp form on the
+    others; keys 128..191 and 320..383 are scaled up so that both kinds of tile
+    (and the growth of the running maximum between them) occur in one row."""
+    w, q, k, v, gkw, okw = inputs(1, 4, 2, 450, 450, 128, "bf16", causal, "none", seed=77)
+    kf = k.float()
+    kf[:, :, 128:192] *= 8.0
+    kf[:, :, 320:384] *= 5.0
+    k = kf.to(torch.bfloat16)
+    print("prefill softcap poly/exact case", causal, cap, flush=True)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), causal, softcap=cap)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), causal, softcap=cap)
+    compare(o, lse, O_ref, L_ref, "bf16", "softcap %g causal %s" % (cap, causal))
+
+
 def test_unbounded_window_and_huge_cap_match_plain():
     """A window wider than the keys and a cap far above every score give the
     plain kernel's result (up to the cap's rounding)."""

@@ -44,3 +44,55 @@ def test_softcap_saturates_without_overflow():
     with np.errstate(over="ignore"):
         got = capped(x, cap, k2)
     assert np.allclose(got, [-cap, -cap, cap, cap, cap], rtol=1e-6)
+
+
+def tanh_poly_coefficients():
+    """The coefficients the prefill kernel's polynomial soft cap uses (attn_kernels.h)."""
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(__file__), "..", "online_softmax_fusion_amd", "csrc",
+                            "attn_kernels.h")).read()
+    m = re.search(r"kTanhPoly\[4\]\s*=\s*\{([^}]*)\}", src)
+    assert m, "kTanhPoly not found"
+    return [float(v.strip().rstrip("f")) for v in m.group(1).split(",")]
+
+
+def fma32(a, b, c):
+    # a * b is exact in float64 for float32 operands; one rounding to float32 after the add
+    return (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
+
+
+@pytest.mark.parametrize("cap_nat", [0.5, 5.0, 20.0, 50.0, 64.0])
+@pytest.mark.parametrize("scale", [0.0883883, 0.125, 1.0, 3.0])
+def test_softcap_polynomial_form(cap_nat, scale):
+    """The polynomial form on the raw score s (what the q @ k product gives):
+    capped (log2 units) = s * P(s^2), P's coefficients scale_log2 * c_i * k^i with
+    k = (scale / softcap)^2, used while |s| <= 0.5 softcap / scale, i.e.
+    |tanh argument| <= 1/2.  Its absolute error stays below 3e-7 of the cap in
+    log2 units (half the exp form's bound), with fp32 evaluation as on the device."""
+    c = tanh_poly_coefficients()
+    sc = np.float32(scale * LOG2E)
+    k = (scale / cap_nat) ** 2
+    q = [np.float32(float(sc) * c[i] * k ** i) for i in range(4)]
+    s0 = 0.5 * cap_nat / scale
+    s = np.concatenate([np.linspace(-s0, s0, 200001), np.logspace(-9, 0, 5000) * s0,
+                        -np.logspace(-9, 0, 5000) * s0]).astype(np.float32)
+    w = (s * s).astype(np.float32)
+    qv = [np.full_like(s, v) for v in q]
+    poly = fma32(fma32(fma32(qv[3], w, qv[2]), w, qv[1]), w, qv[0])
+    got = (s.astype(np.float64) * poly.astype(np.float64)).astype(np.float32).astype(np.float64)
+    cap_l2 = cap_nat * LOG2E
+    exact = cap_l2 * np.tanh(s.astype(np.float64) * scale / cap_nat)
+    err = np.abs(got - exact)
+    assert float(err.max()) <= 3e-7 * cap_l2, (float(err.max()), 3e-7 * cap_l2)
+
+
+def test_tanh_polynomial_range():
+    """The fit itself against tanh on |y| <= 1/2 (1.3e-7 absolute) and its
+    failure well outside (so the kernel's range check is needed)."""
+    c = np.array(tanh_poly_coefficients())
+    y = np.linspace(0, 0.5, 100001)
+    p = y * np.polyval(c[::-1], y * y)
+    assert float(np.abs(p - np.tanh(y)).max()) <= 1.3e-7
+    y2 = np.array([1.5])
+    assert abs(float(y2 * np.polyval(c[::-1], y2 * y2)) - float(np.tanh(y2))) > 1e-3
