@@ -9,7 +9,9 @@ Default run (N = 1):
     roofline: ALiBi causal B=2, H=16, L=8192 (slopes formed in registers); the
     same problem with the ALiBi values given as a bf16 [H, L, L] bias tensor
     broadcast over the batch (bound by HBM: the bias bytes of the visible
-    pairs are read once per batch element); the long causal B=1, H=8, L=32768.
+    pairs are read once per batch element); the long causal B=1, H=8, L=32768;
+    the causal B=4, H=32, L=4096 with a soft cap of 50; the causal B=1, H=8,
+    L=32768 with a sliding window of 4096 keys.
   * decode leg -- the split-K GQA workload B=16, Hq=32, Hkv=8, Lk=32768,
     d=128, 32 chunks of 1024 keys; one step is the local split-K kernel
     followed by the combine.  Reported under "decode" in algorithmic GB/s.
@@ -766,6 +768,7 @@ def traffic_table(d):
                            "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5)}}
     wp, wd, wbk, wl, wll = synth.C2_CAUSAL, synth.C4_DECODE, synth.BWD_PREFILL, synth.L2N_ROWS, synth.L2N_LONG
     w3, w3d, w5, w5d = synth.C3_ALIBI, synth.C3_DENSE, synth.C5_PREFILL, synth.C5_DECODE
+    wsc, wwin = synth.SOFTCAP_PREFILL, synth.WINDOW_PREFILL
     S = wd.splits
     S5 = attn.attn_decode_choose_splits(w5d.B, w5d.Hq, w5d.Hkv, w5d.Lq, w5d.Lk, 256)
     Sl = 128                                        # l2norm_choose_splits for the long rows on 256 CUs
@@ -790,8 +793,14 @@ def traffic_table(d):
          ""),
         ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 8, 12, true>",), w3d, PREFILL_SOURCES,
          pf(w3d) + dense_bias_bytes(w3d), pgrid(w3d), ""),
-        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, ", ", 0, true>"), w5, PREFILL_SOURCES, pf(w5), pgrid(w5),
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 8, 0, true>",), w5, PREFILL_SOURCES, pf(w5), pgrid(w5),
          ""),
+        # soft cap 50 (11: the soft cap for caps up to 64) and the sliding window (four waves, kind 0,
+        # on the long causal grid)
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 4, 11, true>",), wsc, PREFILL_SOURCES, pf(wsc),
+         pgrid(wsc), ""),
+        ("prefill_bf16_kernel", ("prefill_bf16_kernel<128, 4, 0, true>",), wwin, PREFILL_SOURCES, pf(wwin),
+         pgrid(wwin), ""),
         ("decode_bf16_kernel", ("decode_bf16_kernel",), wd, DECODE_SOURCES,
          decode_partial_kernel_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lq, wd.Lk, wd.D, S), S * wd.B * wd.Hkv * 256, ""),
         ("decode_bf16_kernel", ("decode_bf16_kernel",), w5d, DECODE_SOURCES,
@@ -826,8 +835,8 @@ def traffic_table(d):
     return out
 
 
-ALL_LEGS = ("prefill", "prefill_c3", "prefill_c3_dense", "prefill_c5", "decode", "decode_b1", "plan", "l2norm",
-            "backward")
+ALL_LEGS = ("prefill", "prefill_c3", "prefill_c3_dense", "prefill_c5", "prefill_softcap", "prefill_window", "decode",
+            "decode_b1", "plan", "l2norm", "backward")
 
 
 def dense_bias_bytes(w, elem=2) -> int:
@@ -841,7 +850,8 @@ def prefill_leg_json(w, r):
     bias bytes make it bound by HBM, and both fractions are given)."""
     flops = r["flops"]
     kern_tf = flops / r["kern_s"] / 1e12
-    leg = {"workload": w.name, "bias": w.bias, "seed": w.seed, "value": round(flops / r["step_s"] / 1e12, 2),
+    leg = {"workload": w.name, "bias": w.bias, "softcap": w.softcap, "window": list(w.window) if w.window else None,
+           "seed": w.seed, "value": round(flops / r["step_s"] / 1e12, 2),
            "unit": "TFLOP/s",
            "ms_per_step": round(r["step_s"] * 1e3, 4), "kernel_ms": _stats_ms(r["durs"]), "sclk": r["sclk"]}
     traffic = measured_traffic("prefill_bf16_kernel", w.name, PREFILL_SOURCES)
@@ -972,7 +982,8 @@ def main():
         result["roofline"] = leg["roofline"]
         result["kernel_ms"] = leg["kernel_ms"]
         result["sclk"] = leg["sclk"]
-    extra = [("prefill_c3", synth.C3_ALIBI), ("prefill_c3_dense", synth.C3_DENSE), ("prefill_c5", synth.C5_PREFILL)]
+    extra = [("prefill_c3", synth.C3_ALIBI), ("prefill_c3_dense", synth.C3_DENSE), ("prefill_c5", synth.C5_PREFILL),
+             ("prefill_softcap", synth.SOFTCAP_PREFILL), ("prefill_window", synth.WINDOW_PREFILL)]
     pl = [prefill_leg_json(w, time_prefill(w, args.steps, args.warmup, args.warm_seconds))
           for name, w in extra if name in legs]
     if pl:

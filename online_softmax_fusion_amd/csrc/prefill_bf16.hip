@@ -14,7 +14,9 @@
 //      order the P V product wants them.
 //   2. score modifier: without a bias the scale is folded into the exponent
 //      (one FMA per score: t = s * scale * log2(e) - m); with a bias the score
-//      is formed first, t = s * scale * log2(e) + bias * log2(e).  The causal
+//      is formed first, t = s * scale * log2(e) + bias * log2(e); the soft cap
+//      c tanh(t / c) is a polynomial in s where every score of the tile is
+//      within |t| <= c / 2, else formed through 2^(2t / c).  The causal
 //      mask and the key tail are applied only on tiles that cross them (a
 //      separate code path, so full tiles carry no compare at all).
 //   3. rolling update (Neptune notes section 3 and section 4): the row max
@@ -91,10 +93,11 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                                              int jmin, int jmax, float slope_l2, int b, int h, int lane) {
     using C = TileCfg<D>;
     constexpr bool AC = (BIAS == kBiasAlibiCausal);
-    // CE: the soft cap by the exp form with a positive scale: the capped score
-    // is increasing in the raw one, so the tile max is taken on raw scores and
-    // capped once, and P = 2^(c - m - 2c / (2^(s * scale * k2) + 1)) is formed
-    // from the raw score directly
+    // CE: the soft cap for caps up to 64 with a positive scale: the capped
+    // score is increasing in the raw one, so a tile max is taken on raw scores
+    // and capped once, and P is formed from the raw score directly, as
+    // 2^(s P(s^2) - m) (the polynomial form, on unmasked tiles whose raw scores
+    // all lie within cap_s0) or 2^(c - m - 2c / (2^(s * scale * k2) + 1))
     constexpr bool CE = (BIAS == kBiasNoneCapExp);
     constexpr bool FOLD = (BIAS == kBiasNone) || AC || CE;
     constexpr int BK = bias_base(BIAS);
