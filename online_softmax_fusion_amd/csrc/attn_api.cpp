@@ -131,8 +131,14 @@ FwdParams make_params(const attn_fwd_args *a) {
         if (a->scale > 0.f) {
             const double k = ((double)a->scale / a->softcap) * ((double)a->scale / a->softcap);
             double kp = 1.0;
-            for (int i = 0; i < 4; ++i, kp *= k) p.cap_q[i] = (float)((double)p.scale_log2 * attn::kTanhPoly[i] * kp);
-            p.cap_s0 = (float)(0.5 * a->softcap / a->scale);
+            bool finite = true;
+            for (int i = 0; i < 4; ++i, kp *= k) {
+                p.cap_q[i] = (float)((double)p.scale_log2 * attn::kTanhPoly[i] * kp);
+                finite = finite && std::isfinite(p.cap_q[i]);
+            }
+            // a cap so small against the scale that the coefficients leave the
+            // float range: every tile takes the exp form (|s| > -1 always)
+            p.cap_s0 = finite ? (float)(0.5 * a->softcap / a->scale) : -1.f;
         }
     }
     p.window = a->window;

@@ -256,6 +256,18 @@ def test_prefill_softcap_polynomial_and_exact_tiles(causal, cap):
     compare(o, lse, O_ref, L_ref, "bf16", "softcap %g causal %s" % (cap, causal))
 
 
+def test_prefill_tiny_softcap():
+    """A cap so small against the scale (1e-8) that the polynomial's scaled
+    coefficients leave the float range: every tile takes the exp form, and
+    the rows average the values they see."""
+    w, q, k, v, gkw, okw = inputs(1, 2, 2, 200, 200, 128, "bf16", True, "none", seed=78)
+    print("prefill tiny softcap", flush=True)
+    o, lse = attn.attn_fwd_prefill(q.cuda(), k.cuda(), v.cuda(), w.softmax_scale(), True, softcap=1e-8)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(q, k, v, w.softmax_scale(), True, softcap=1e-8)
+    compare(o, lse, O_ref, L_ref, "bf16", "softcap 1e-8")
+
+
 def test_unbounded_window_and_huge_cap_match_plain():
     """A window wider than the keys and a cap far above every score give the
     plain kernel's result (up to the cap's rounding)."""
