@@ -196,7 +196,13 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                 if (BK == kBiasDenseBf16Tiled && (e & 7) == 0)
                     bch = load16(lb + (bbase ^ ((4 * kb + 2 * (e >> 3) + hh) << 4)));
                 float x = s[kb][e];
-                if (!FOLD) {
+                if (BK == kBiasDenseBf16Tiled) {
+                    // natural units, scale and bias in one FMA; the exponent
+                    // takes log2(e)
+                    const uint32_t wv = bch[(e & 7) >> 1];
+                    const float bv = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+                    x = fmaf(x, p.scale, bv);
+                } else if (!FOLD) {
                     x *= sc;
                     if (CAP) {   // in log2 units
                         if constexpr (BIAS == kBiasNoneCapExp)
@@ -206,10 +212,6 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                     }
                     if (BK == kBiasAlibi) {
                         x = fmaf(-slope_l2, fabsf(dbase - (float)(kb * 32 + (e >> 3) * 16 + (e & 7))), x);
-                    } else if (BK == kBiasDenseBf16Tiled) {
-                        const uint32_t wv = bch[(e & 7) >> 1];
-                        const float bv = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
-                        x = fmaf(bv, kLog2e, x);
                     } else if (BK == kBiasDenseF32 || BK == kBiasDenseBf16) {
                         const int bi = min(qrow, p.Lq - 1);
                         const int bj = min(j, p.Lk - 1);
@@ -253,6 +255,9 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
                 } else if (FOLD) {
                     p0 = exp2_fast(fmaf(s[kb][e], sc, -m_use));
                     p1 = exp2_fast(fmaf(s[kb][e + 1], sc, -m_use));
+                } else if (BK == kBiasDenseBf16Tiled) {
+                    p0 = exp2_fast(fmaf(s[kb][e], kLog2e, -m_use));
+                    p1 = exp2_fast(fmaf(s[kb][e + 1], kLog2e, -m_use));
                 } else {
                     p0 = exp2_fast(s[kb][e] - m_use);
                     p1 = exp2_fast(s[kb][e + 1] - m_use);
@@ -346,6 +351,7 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     } else {
         float mx = xor32_max(modify());
         if (FOLD) mx *= sc;   // sc > 0: max commutes with the scaling
+        if (BK == kBiasDenseBf16Tiled) mx *= kLog2e;
         // 3. lazy repair of l and O when the max has grown by more than TAU
         if (__any(mx > m_run + kTau)) repair(fmaxf(m_run, mx));
         // 4. P = 2^(t - m) in fp32, summed in fp32, packed to bf16
@@ -457,8 +463,12 @@ __device__ __forceinline__ void prefill_body(const FwdParams &p) {
     const WorkItem wi = xcd_work_item(nqt, p.causal && !p.window, p.num_xcds);
     const int bh = wi.head;
     const int qt = p.causal ? nqt - 1 - wi.rank : wi.rank;
-    const int b = bh / p.Hq;
-    const int h = bh - b * p.Hq;
+    // a tiled bias shared by the batch: the batch elements of one head are
+    // neighbours in the work order, so they run on one XCD at the same time and
+    // the second reads each bias tile from that XCD's L2
+    const bool bfirst = TB && p.bias_sb == 0 && p.B > 1;
+    const int b = bfirst ? bh % p.B : bh / p.Hq;
+    const int h = bfirst ? bh / p.B : bh - b * p.Hq;
     const int hk = h / p.G;
     const int q0 = qt * BR;
 

@@ -137,9 +137,10 @@ def test_prefill_eight_wave_sampled(case):
 # bf16 dense bias at d = 128: rows of contiguous keys that start 16-byte
 # aligned are loaded a tile at a time into LDS beside K and V (eight-wave
 # workgroups); other layouts read each element where it is used.  Layouts:
-# contiguous [Hq, Lq, Lk]; rows padded to a longer stride (the keys past Lk in
-# a row's last chunk are padding); one [Lq, Lk] plane broadcast over batch and
-# heads; rows whose stride is not a multiple of 8 elements (the per-element path).
+# contiguous [Hq, Lq, Lk] (shared by the batch); rows padded to a longer stride
+# (the keys past Lk in a row's last chunk are padding); one [Lq, Lk] plane
+# broadcast over batch and heads; a plane per batch element; rows whose stride
+# is not a multiple of 8 elements (the per-element path).
 DENSE_BF16_CASES = [
     # B, Hq, Hkv, Lq, Lk, causal, layout
     (2, 4, 2, 300, 328, True, "contiguous"),
@@ -148,6 +149,8 @@ DENSE_BF16_CASES = [
     (1, 2, 2, 600, 200, True, "contiguous"),    # Lq > Lk: rows that see no key
     (1, 2, 2, 100, 333, False, "contiguous"),   # stride of 333 elements: per-element path
     (1, 2, 2, 1, 64, False, "contiguous"),
+    (3, 2, 2, 260, 264, False, "contiguous"),   # three batch elements share the bias (work order)
+    (2, 2, 2, 260, 264, True, "batched"),       # [B, Hq, Lq, Lk]: a bias plane per batch element
 ]
 
 
@@ -159,6 +162,8 @@ def test_prefill_dense_bf16_layouts(case):
     q, k, v = synth.make_qkv(w)
     if layout == "broadcast":
         bt = synth.make_dense_bias(w, (Lq, Lk), "bf16")
+    elif layout == "batched":
+        bt = synth.make_dense_bias(w, (B, Hq, Lq, Lk), "bf16")
     elif layout == "padded":
         bt = synth.make_dense_bias(w, (Hq, Lq, Lk + 6), "bf16")[..., :Lk]
     else:
