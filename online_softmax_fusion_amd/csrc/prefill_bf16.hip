@@ -184,7 +184,8 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
     u32x4 bch{};
     // ALiBi distance qpos - j = dbase - (a compile-time offset of the element)
     const float dbase = (float)(qpos - kt0 - hh * 8);
-    // the score modifier in place (log2 units unless the scale is folded),
+    // the score modifier in place (log2 units; raw scores where the scale is
+    // folded into the exponent, natural units with the tiled dense bias),
     // masked keys set to -inf; returns this lane's maximum
     auto modify = [&]() {
         float mx = -INFINITY;
@@ -233,7 +234,8 @@ __device__ __forceinline__ void process_tile(const FwdParams &p, const char *lk,
         return mx;
     };
 
-    // weights P = 2^(t - m_use) in fp32, packed to bf16; returns this lane's sum
+    // weights P = 2^(t - m_use) in fp32, packed to bf16, t the score in log2
+    // units (formed here from the units modify leaves); returns this lane's sum
     uint32_t pk[2][8];
     auto weights = [&](float m_use) {
         float lt = 0.f;
